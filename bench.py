@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MoE decode layer (W4A8: MXFP4 experts, FP8 activations).
+
+Workload: the Ling-shaped decode layer (hidden 2560, expert intermediate 768,
+256 experts, top-8) streamed cold: 40 independent layers (about 30 GiB of MXFP4
+weights, far above the 256 MB Infinity Cache) are walked in turn, every layer
+with its own freshly drawn hidden state, so no layer's weights are cache-warm
+when it runs.  One step = one layer forward (router, top-K, compaction, FP8
+quantisation, gate/up + SiLU + requantisation, down + combine) through the C
+ABI.  The walk of 40 layers is captured once per hidden set in a HIP graph and
+replayed; plain launches are timed too.
+
+Reported (one JSON line on stdout):
+  value        algorithmic HBM GB/s at 1 token (bytes the layer must read or
+               write: the 8 selected experts' MXFP4 codes and scales, the bf16
+               router, x and out) / wall time
+  us_per_layer wall time per layer
+  m4           the same at 4 tokens (the speculative-decoding verify window)
+  roofline     the gate/up kernel (the largest byte stream) against 8 TB/s,
+               from HIP events recorded around it inside the replayed graphs
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+H, I, E, K = 2560, 768, 256, 8
+HBM_PEAK_GBS = 8000.0
+W13_BYTES = 2 * I * H // 2 + 2 * I * H // 32          # codes + E8M0 scales of one expert's gate/up
+W2_BYTES = H * I // 2 + H * I // 32
+EXPERT_BYTES = W13_BYTES + W2_BYTES                     # 3,133,440
+ROUTER_BYTES = E * H * 2
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_bytes(n_act: int, M: int) -> int:
+    return n_act * EXPERT_BYTES + ROUTER_BYTES + M * H * 2 + M * H * 4
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20000, help="timed layer forwards (rounded up to whole walks)")
+    p.add_argument("--warmup", type=int, default=2000)
+    p.add_argument("--layers", type=int, default=40)
+    p.add_argument("--reps", type=int, default=8, help="independent hidden sets (one graph each)")
+    p.add_argument("--plain-steps", type=int, default=2000, help="layer forwards timed with plain launches")
+    p.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU baseline (0: skip)")
+    return p.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer is not sharded "
+              "across GPUs in this library)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mxfp4_weight_streaming_amd import binding as moe
+    from mxfp4_weight_streaming_amd import synth
+
+    torch.cuda.set_device(0)
+    shp = moe.shape(H, I, E, K)
+    L, reps = args.layers, args.reps
+    st, path = moe.moe_path_info(shp, 1)
+    assert st == 0, path
+    log(f"path: {path}")
+    log(f"drawing {L} layers of weights on the GPU ({L * (EXPERT_BYTES * E + ROUTER_BYTES) / 2**30:.1f} GiB)")
+    stack = synth.device_stack(L, H, I, E, seed=1234)
+    stream = torch.cuda.Stream()
+    ws = moe.workspace(shp, 8)
+    out = torch.empty((8, H), dtype=torch.float32, device="cuda")
+
+    def fwd(l, x, M, events=None):
+        Ly = stack[l]
+        if events is None:
+            moe.moe_decode_forward(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws)
+        else:
+            moe.moe_decode_forward_events(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws,
+                                          events)
+
+    results = {}
+    kernel_stats = {}
+    for M in (1, 4):
+        xs = synth.device_hidden(L * reps, M, H, seed=10_000 + M)
+        # routing pre-pass: distinct experts of every (hidden set, layer)
+        ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
+        wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
+        n_active = torch.empty(1, dtype=torch.int32, device="cuda")
+        n_act = np.zeros((reps, L), np.int64)
+        with torch.cuda.stream(stream):
+            for r in range(reps):
+                for l in range(L):
+                    moe.moe_route(shp, M, xs[r * L + l], stack[l]["wr"], ids, wts, ws, taps={"n_active": n_active})
+                    n_act[r, l] = int(n_active.item())
+        rep_bytes = [sum(layer_bytes(int(n_act[r, l]), M) for l in range(L)) for r in range(reps)]
+
+        with torch.cuda.stream(stream):
+            for r in range(reps):                                  # eager warm-up walk of every set
+                for l in range(L):
+                    fwd(l, xs[r * L + l], M)
+            torch.cuda.synchronize()
+            graphs = []
+            for r in range(reps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for l in range(L):
+                        fwd(l, xs[r * L + l], M)
+                graphs.append(g)
+        n_warm = max(1, math.ceil(args.warmup / L))
+        n_timed = max(1, math.ceil(args.steps / L))
+        with torch.cuda.stream(stream):
+            for i in range(n_warm):
+                graphs[i % reps].replay()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            wall0 = time.perf_counter()
+            t0.record(stream)
+            for i in range(n_timed):
+                graphs[i % reps].replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - wall0
+        ms = t0.elapsed_time(t1)
+        steps = n_timed * L
+        total_bytes = sum(rep_bytes[i % reps] for i in range(n_timed))
+        gbs = total_bytes / (ms * 1e-3) / 1e9
+        log(f"M={M}: graph replay {steps} layers in {ms:.2f} ms ({ms * 1e3 / steps:.2f} us/layer, {gbs:.0f} GB/s, "
+            f"host wall {wall * 1e3:.1f} ms), mean distinct experts {n_act.mean():.2f}")
+
+        # plain launches (no graph)
+        n_plain = max(L, args.plain_steps)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            p0 = torch.cuda.Event(enable_timing=True)
+            p1 = torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            pbytes = 0
+            for i in range(n_plain):
+                r, l = (i // L) % reps, i % L
+                fwd(l, xs[r * L + l], M)
+                pbytes += layer_bytes(int(n_act[r, l]), M)
+            p1.record(stream)
+            torch.cuda.synchronize()
+        pms = p0.elapsed_time(p1)
+
+        # per-kernel durations from HIP events recorded between the kernels of
+        # each layer, in plain launches; a spin kernel at the head of the
+        # stream lets the host queue the whole walk first, so the kernels run
+        # back to back and the events see no host gaps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+        dur = {"router": [], "gate_up": [], "down": []}
+        with torch.cuda.stream(stream):
+            for row in evs:
+                for e in row:
+                    e.record(stream)          # torch creates the HIP event on first record
+            for ps in range(max(2, 400 // L)):
+                torch.cuda._sleep(50_000_000)
+                r = ps % reps
+                for l in range(L):
+                    fwd(l, xs[r * L + l], M, events=evs[l])
+                torch.cuda.synchronize()
+                for l in range(L):
+                    dur["router"].append(evs[l][0].elapsed_time(evs[l][1]))
+                    dur["gate_up"].append(evs[l][1].elapsed_time(evs[l][2]))
+                    dur["down"].append(evs[l][2].elapsed_time(evs[l][3]))
+        kmean = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}   # microseconds
+        gu_bytes = float(np.mean(n_act[0])) * W13_BYTES
+        kernel_stats[M] = {"us": kmean, "gate_up_bytes": gu_bytes,
+                           "gate_up_gbs": gu_bytes / (kmean["gate_up"] * 1e-6) / 1e9}
+        log(f"M={M}: kernel means (us) {kmean}, gate_up {kernel_stats[M]['gate_up_gbs']:.0f} GB/s")
+
+        results[M] = {"us_per_layer": ms * 1e3 / steps, "gbs": gbs, "steps": steps, "ms": ms,
+                      "mean_distinct_experts": float(n_act.mean()),
+                      "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9}
+        del graphs, xs
+
+    cpu = None
+    if args.cpu_layers > 0:
+        cpu = cpu_baseline(args.cpu_layers)
+
+    r1, r4 = results[1], results[4]
+    k1 = kernel_stats[1]
+    line = {
+        "metric": "MoE-layer decode us + weight-stream HBM GB/s (% of peak), M=1 and M=4",
+        "value": round(r1["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r1["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": r1["ms"] / r1["steps"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 x e4m3 -> f32",
+        "data": "synthetic",
+        "config": {"workload": "ling-shaped MoE decode layer, 1 token, cold walk over 40 layers",
+                   "hidden": H, "expert_inter": I, "experts": E, "topk": K, "tokens": 1, "layers": L,
+                   "launch": "hip graph per 40-layer walk"},
+        "us_per_layer": round(r1["us_per_layer"], 3),
+        "pct_of_hbm_peak": round(100 * r1["gbs"] / HBM_PEAK_GBS, 2),
+        "plain_launch": {"us_per_layer": round(r1["plain_us_per_layer"], 3), "gbs": round(r1["plain_gbs"], 1)},
+        "m4": {"us_per_layer": round(r4["us_per_layer"], 3), "gbs": round(r4["gbs"], 1),
+               "pct_of_hbm_peak": round(100 * r4["gbs"] / HBM_PEAK_GBS, 2),
+               "mean_distinct_experts": round(r4["mean_distinct_experts"], 2),
+               "plain_us_per_layer": round(r4["plain_us_per_layer"], 3),
+               "kernel_us": {k: round(v, 3) for k, v in kernel_stats[4]["us"].items()},
+               "gate_up_gbs": round(kernel_stats[4]["gate_up_gbs"], 1)},
+        "kernel_us": {k: round(v, 3) for k, v in k1["us"].items()},
+        "roofline": {"kernel": "gate_up_kernel<H=2560,I=768> (1 token)", "bound": "hbm",
+                     "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(n_layers: int) -> dict:
+    """The oracle, single-threaded, on n_layers Ling-shaped 1-token layers."""
+    import numpy as np
+
+    import oracle
+    from mxfp4_weight_streaming_amd import synth
+    log(f"cpu baseline: oracle on {n_layers} layers")
+    w = synth.expert_weights(77, H, I, E)
+    oracle.lib()
+    total = 0
+    t0 = time.perf_counter()
+    for i in range(n_layers):
+        rng = np.random.default_rng(500 + i)
+        wr = synth.normal_bf16(rng, (E, H), 0.02)
+        x = synth.normal_bf16(rng, (1, H), 1.0)
+        oracle.moe_layer(x, wr, w.w13, w.s13, w.w2, w.s2, K)
+        total += layer_bytes(K, 1)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {dt:.1f} s")
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_layers} Ling-shaped 1-token layers (H=2560, I=768, E=256, K=8), "
+                      f"{dt / n_layers * 1e3:.0f} ms per layer on one host core"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,213 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) W4A8 mixture-of-experts decode layer.
+ *
+ * What the layer computes.  The pages behind this library describe decode of
+ * a Ling-3.0-flash-shaped MoE model at batch size 1 and find it bound by
+ * reading weights; the two largest readers are the MoE experts and the LM
+ * head ([EN] "Why is MoE decoding on DGX Spark memory-bound?"; [ZH]
+ * "三项优化分别做了什么").  The model routes every token to 8 routed experts
+ * ([EN] "What is Ling 3.0, and why does it suit DGX Spark?"), its expert
+ * layer is 768 wide ([EN] "What are the 3 optimizations?", item 1), its hidden
+ * state is 2,560 wide (same section, item 2), the experts are stored as MXFP4
+ * with FP8 activations (the W4A8 recipe, [EN] "Why is MoE decoding...") and a
+ * speculative-decoding verify step runs 4 token positions through the layer at
+ * once, touching up to 32 experts ([EN] "What are the 3 optimizations?",
+ * item 3; [ZH] "合成负载与真实评测的差距").
+ *   [EN] = "NVIDIA Shows 3 Ways to Speed Up MoE Inference on DGX Spark,
+ *          Lifting Ling-3.0-flash Throughput 42.5%"
+ *   [ZH] = "NVIDIA博客:DGX Spark上三项优化使Ling-3.0-flash解码吞吐提升 42.5%"
+ *
+ * For M tokens x[M,H] (bf16), E experts and top-K routing:
+ *   logits = x Wr^T (fp32); ids = the K largest logits per token (ties -> lower
+ *   expert index); w = softmax restricted to the K selected logits.
+ *   q, s   = per-token FP8 E4M3 quantisation: s = amax/448 (1 if amax == 0),
+ *            q = E4M3_RNE_satfinite(x / s) with a correctly rounded fp32 division.
+ *   for each (token t, rank j), expert e = ids[t,j], pair p = t*K + j:
+ *     g, u = rows [0,I) and [I,2I) of W13[e] times A = E4M3(q[t]) * s[t]
+ *     h[p] = SiLU(g) * u                         (fp32; SiLU(z) = z * sigmoid(z))
+ *     s2[p] = max|h[p]| / 448 (1 if 0); q2[p] = E4M3_RNE_satfinite(h[p] / s2[p])
+ *   out[t] = sum_j w[t,j] * s2[p] * (W2[e] times E4M3(q2[p]))   (fp32, overwritten)
+ * where an MXFP4 matrix element is E2M1(code) * 2^(E8M0 block scale - 127).
+ * No residual and no shared expert are added.
+ *
+ * Storage layout (every tensor dense, row-major, no padding):
+ *   hidden      bf16 bits  [M, H]
+ *   router_w    bf16 bits  [E, H]
+ *   w13         u8         [E, 2I, H/2]   E2M1 codes; element 2i in bits 3:0 of
+ *                                          byte i, element 2i+1 in bits 7:4;
+ *                                          rows [0,I) gate, rows [I,2I) up
+ *   w13_scale   u8 (E8M0)  [E, 2I, H/32]  one scale per 32 consecutive elements
+ *   w2          u8         [E, H, I/2]    same nibble order
+ *   w2_scale    u8 (E8M0)  [E, H, I/32]
+ *   out         fp32       [M, H]
+ *   act_fp8     u8 (E4M3)  [M, H],  act_scale fp32 [M]
+ *   topk_ids    int32      [M, K],  topk_w    fp32 [M, K]   (pair p = t*K + j)
+ *   inter_fp8   u8 (E4M3)  [M*K, I], inter_scale fp32 [M*K], h fp32 [M*K, I]
+ *
+ * Ownership and execution.  Every tensor pointer is device memory owned by
+ * the caller.  The library never allocates, frees or synchronises: each call
+ * validates its arguments on the host, enqueues its kernels on `stream`
+ * (a hipStream_t; NULL is the default stream) and returns.  The caller keeps
+ * every buffer alive until the stream has passed the call.  Inputs are only
+ * read.  A workspace serves one call in flight at a time; calls with distinct
+ * workspaces may run concurrently.  The library keeps no other global state
+ * except a thread-local copy of the last error message.
+ *
+ * Errors.  Every argument is checked before anything is enqueued; on any
+ * error nothing is enqueued and the status says why.  No C++ exception
+ * crosses this interface.  A shape outside the compiled set is
+ * MOE_ERR_UNSUPPORTED_SHAPE -- there is never a silent fallback to a slower
+ * or different kernel (the pages warn that a silent fallback made a draft
+ * model misread FP8 weights as BF16: [EN] "What are the 3 optimizations?",
+ * "The integration trap"; [ZH] "叠加时的配置陷阱").  moe_path_info() names the
+ * kernels a call would run so that callers can check at startup that the path
+ * they expect is active, as the pages advise.  Non-finite inputs are not
+ * detected; results for them are unspecified.  Caller-given topk_ids must
+ * lie in [0, E) and be distinct within a token; other ids give unspecified
+ * results (they are clamped on the device, never read or written out of
+ * bounds).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,       /* null pointer, non-positive size, K > E ... */
+    MOE_ERR_UNSUPPORTED_SHAPE = -2, /* (H, I, E, K, M) outside the compiled set  */
+    MOE_ERR_ALIGNMENT = -3,         /* a tensor base is not 16-byte aligned       */
+    MOE_ERR_WORKSPACE = -4,         /* workspace missing, misaligned or too small */
+    MOE_ERR_HIP = -5                /* a HIP launch or copy failed                */
+} moe_status;
+
+/* H = hidden, I = expert intermediate, E = routed experts, K = experts per token. */
+typedef struct {
+    int32_t hidden;
+    int32_t inter;
+    int32_t num_experts;
+    int32_t topk;
+} moe_shape;
+
+/* Optional device outputs of moe_route for checking the routing stages.
+ * Any member may be NULL.  Sizes use S = min(E, M*K). */
+typedef struct {
+    float*   logits;       /* [M, E] fp32 router logits                              */
+    int32_t* n_active;     /* [1] number of distinct selected experts                */
+    int32_t* act_experts;  /* [S] distinct selected experts, ascending id            */
+    int32_t* offsets;      /* [S+1] start of each expert's pair list                 */
+    int32_t* pair_token;   /* [M*K] token of each compacted pair                     */
+    int32_t* pair_src;     /* [M*K] pair index t*K+j of each compacted pair          */
+    uint8_t* act_fp8;      /* [M, H] E4M3 activations, as the router kernel makes them */
+    float*   act_scale;    /* [M] their fp32 scales                                   */
+} moe_route_taps;
+
+/* Optional device outputs of the expert stages.  Any member may be NULL. */
+typedef struct {
+    float*   h;            /* [M*K, I] fp32 SiLU(g)*u before requantisation          */
+    uint8_t* inter_fp8;    /* [M*K, I] E4M3 intermediate                              */
+    float*   inter_scale;  /* [M*K] fp32 intermediate scale                           */
+} moe_expert_taps;
+
+/* Bytes of workspace needed for calls with up to max_tokens tokens; 0 if the
+ * shape or max_tokens is invalid or unsupported.  The requirement is
+ * non-decreasing in max_tokens, so one workspace sized for max_tokens serves
+ * every smaller M. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens);
+
+/* Zero the workspace (a fill kernel on `stream`; the caller orders later
+ * calls on other streams after it).  Call once after allocating a workspace;
+ * later calls keep its control block clean themselves.  ws must be 256-byte
+ * aligned. */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer for M tokens: route -> quantise -> compact -> gate/up ->
+ * requantise -> down + combine.  out[M,H] fp32 is overwritten. */
+moe_status moe_decode_forward(const moe_shape* shape, int32_t M,
+                              const uint16_t* hidden, const uint16_t* router_w,
+                              const uint8_t* w13, const uint8_t* w13_scale,
+                              const uint8_t* w2, const uint8_t* w2_scale,
+                              float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_decode_forward that also records caller-created HIP events on `stream`
+ * for per-kernel timing: events[0] before the router kernel, events[1] after
+ * it, events[2] after the gate/up kernel, events[3] after the requantisation
+ * and down kernels.
+ * `events` (an array of 4 hipEvent_t) or any element may be NULL.  Usable
+ * under stream capture (the records become graph event nodes). */
+moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M,
+                                     const uint16_t* hidden, const uint16_t* router_w,
+                                     const uint8_t* w13, const uint8_t* w13_scale,
+                                     const uint8_t* w2, const uint8_t* w2_scale,
+                                     float* out, void* ws, size_t ws_bytes, void* stream,
+                                     void* const* events);
+
+/* Router, top-K, renormalised weights and compaction (the first kernel of
+ * moe_decode_forward; it also quantises the activations when the taps ask
+ * for them).  topk_ids/topk_w [M,K] are written in canonical order (logit
+ * descending, expert index ascending).  taps may be NULL. */
+moe_status moe_route(const moe_shape* shape, int32_t M,
+                     const uint16_t* hidden, const uint16_t* router_w,
+                     int32_t* topk_ids, float* topk_w, const moe_route_taps* taps,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token FP8 E4M3 activation quantisation as a kernel of its own (the
+ * router kernel produces the same bytes; see moe_route_taps).  No workspace. */
+moe_status moe_quant_act(const moe_shape* shape, int32_t M, const uint16_t* hidden,
+                         uint8_t* act_fp8, float* act_scale, void* stream);
+
+/* Everything after routing, on caller-given routing (e.g. an oracle's ids and
+ * weights for tokens whose K-th and (K+1)-th logits are too close to call):
+ * compaction -> gate/up -> requantise -> down + combine.  taps may be NULL. */
+moe_status moe_experts_forward(const moe_shape* shape, int32_t M,
+                               const uint8_t* act_fp8, const float* act_scale,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const uint8_t* w13, const uint8_t* w13_scale,
+                               const uint8_t* w2, const uint8_t* w2_scale,
+                               float* out, const moe_expert_taps* taps,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Compaction and the fused gate/up kernel alone: writes h, the E4M3
+ * intermediate and its scales.  All three outputs are required. */
+moe_status moe_gate_up(const moe_shape* shape, int32_t M,
+                       const uint8_t* act_fp8, const float* act_scale,
+                       const int32_t* topk_ids,
+                       const uint8_t* w13, const uint8_t* w13_scale,
+                       float* h, uint8_t* inter_fp8, float* inter_scale,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Compaction and the down-projection + combine kernel alone, on a
+ * caller-given E4M3 intermediate [M*K, I] and scales [M*K]. */
+moe_status moe_down_combine(const moe_shape* shape, int32_t M,
+                            const uint8_t* inter_fp8, const float* inter_scale,
+                            const int32_t* topk_ids, const float* topk_w,
+                            const uint8_t* w2, const uint8_t* w2_scale,
+                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The E4M3 encoder the quantisation kernels use, applied to the n binary32
+ * values whose bit patterns are first_bits, first_bits+1, ... (wrapping at
+ * 2^32): q[i] = E4M3_RNE_satfinite(bits_as_float(first_bits + i)).  For
+ * exhaustive checks of the encoder. */
+moe_status moe_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* q, void* stream);
+
+/* Writes a one-line description of the kernels a call with this shape and M
+ * would run (NUL-terminated, truncated to len).  Returns the same status the
+ * call's shape validation would. */
+moe_status moe_path_info(const moe_shape* shape, int32_t M, char* buf, size_t len);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status status);
+
+/* The last error message recorded on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

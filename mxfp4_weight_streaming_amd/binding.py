@@ -1,0 +1,220 @@
+"""ctypes binding of libmoe_decode.so (the C ABI in include/moe_decode.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library.  Tensors are passed as device pointers (``tensor.data_ptr()``),
+streams as ``hipStream_t`` handles (default: torch's current stream).  Importing
+this module fails loudly if the library has not been built; there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_decode.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_decode.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; build it with `python -m mxfp4_weight_streaming_amd.build` "
+        "(hipcc, gfx950). The MoE layer has no non-HIP implementation.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED_SHAPE = -2
+MOE_ERR_ALIGNMENT = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("topk", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"MoeShape(H={self.hidden}, I={self.inter}, E={self.num_experts}, K={self.topk})"
+
+
+class MoeRouteTaps(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("n_active", ctypes.c_void_p), ("act_experts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("pair_token", ctypes.c_void_p), ("pair_src", ctypes.c_void_p),
+                ("act_fp8", ctypes.c_void_p), ("act_scale", ctypes.c_void_p)]
+
+
+class MoeExpertTaps(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("inter_fp8", ctypes.c_void_p), ("inter_scale", ctypes.c_void_p)]
+
+
+_V = ctypes.c_void_p
+_S = ctypes.POINTER(MoeShape)
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_workspace_bytes": (_sz, [_S, _i32]),
+    "moe_workspace_init": (ctypes.c_int, [_V, _sz, _V]),
+    "moe_decode_forward": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
+    "moe_decode_forward_events": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V,
+                                                  ctypes.POINTER(ctypes.c_void_p)]),
+    "moe_route": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, ctypes.POINTER(MoeRouteTaps), _V, _sz, _V]),
+    "moe_quant_act": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V]),
+    "moe_experts_forward": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                           ctypes.POINTER(MoeExpertTaps), _V, _sz, _V]),
+    "moe_gate_up": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
+    "moe_down_combine": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
+    "moe_fp8_encode_range": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_int64, _V, _V]),
+    "moe_path_info": (ctypes.c_int, [_S, _i32, ctypes.c_char_p, _sz]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/moe_decode.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.moe_last_error().decode()
+        super().__init__(f"{where}: {_lib.moe_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(status: int, where: str) -> int:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+    return status
+
+
+def _p(t):
+    """Device pointer of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def shape(hidden: int, inter: int, num_experts: int, topk: int) -> MoeShape:
+    return MoeShape(hidden, inter, num_experts, topk)
+
+
+def moe_workspace_bytes(shp: MoeShape, max_tokens: int) -> int:
+    return _lib.moe_workspace_bytes(ctypes.byref(shp), max_tokens)
+
+
+def moe_workspace_init(ws, stream=None) -> None:
+    _check(_lib.moe_workspace_init(_p(ws), _nbytes(ws), _stream(stream)), "moe_workspace_init")
+
+
+def workspace(shp: MoeShape, max_tokens: int, device="cuda"):
+    """Allocate (through torch) and initialise a workspace for up to max_tokens."""
+    import torch
+    n = moe_workspace_bytes(shp, max_tokens)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED_SHAPE, "moe_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_workspace_init(ws)
+    torch.cuda.current_stream().synchronize()   # usable from any stream afterwards
+    return ws
+
+
+def moe_decode_forward(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, stream=None):
+    _check(_lib.moe_decode_forward(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
+                                   _p(w2), _p(w2_scale), _p(out), _p(ws), _nbytes(ws), _stream(stream)),
+           "moe_decode_forward")
+
+
+def moe_decode_forward_events(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, events,
+                              stream=None):
+    """events: 4 torch.cuda.Event (or None entries); recorded around the 3 kernels."""
+    arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+    _check(_lib.moe_decode_forward_events(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
+                                          _p(w2), _p(w2_scale), _p(out), _p(ws), _nbytes(ws), _stream(stream),
+                                          arr),
+           "moe_decode_forward_events")
+
+
+def moe_route(shp, M, hidden, router_w, topk_ids, topk_w, ws, taps: dict | None = None, stream=None):
+    t = None
+    if taps is not None:
+        t = MoeRouteTaps(*[_p(taps.get(k)) for k, _ in MoeRouteTaps._fields_])
+    _check(_lib.moe_route(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(topk_ids), _p(topk_w),
+                          ctypes.byref(t) if t is not None else None, _p(ws), _nbytes(ws), _stream(stream)),
+           "moe_route")
+
+
+def moe_quant_act(shp, M, hidden, act_fp8, act_scale, stream=None):
+    _check(_lib.moe_quant_act(ctypes.byref(shp), M, _p(hidden), _p(act_fp8), _p(act_scale), _stream(stream)),
+           "moe_quant_act")
+
+
+def moe_experts_forward(shp, M, act_fp8, act_scale, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out, ws,
+                        taps: dict | None = None, stream=None):
+    t = None
+    if taps is not None:
+        t = MoeExpertTaps(*[_p(taps.get(k)) for k, _ in MoeExpertTaps._fields_])
+    _check(_lib.moe_experts_forward(ctypes.byref(shp), M, _p(act_fp8), _p(act_scale), _p(topk_ids), _p(topk_w),
+                                    _p(w13), _p(w13_scale), _p(w2), _p(w2_scale), _p(out),
+                                    ctypes.byref(t) if t is not None else None, _p(ws), _nbytes(ws),
+                                    _stream(stream)),
+           "moe_experts_forward")
+
+
+def moe_gate_up(shp, M, act_fp8, act_scale, topk_ids, w13, w13_scale, h, inter_fp8, inter_scale, ws, stream=None):
+    _check(_lib.moe_gate_up(ctypes.byref(shp), M, _p(act_fp8), _p(act_scale), _p(topk_ids), _p(w13),
+                            _p(w13_scale), _p(h), _p(inter_fp8), _p(inter_scale), _p(ws), _nbytes(ws),
+                            _stream(stream)),
+           "moe_gate_up")
+
+
+def moe_down_combine(shp, M, inter_fp8, inter_scale, topk_ids, topk_w, w2, w2_scale, out, ws, stream=None):
+    _check(_lib.moe_down_combine(ctypes.byref(shp), M, _p(inter_fp8), _p(inter_scale), _p(topk_ids), _p(topk_w),
+                                 _p(w2), _p(w2_scale), _p(out), _p(ws), _nbytes(ws), _stream(stream)),
+           "moe_down_combine")
+
+
+def moe_fp8_encode_range(first_bits: int, n: int, q, stream=None):
+    _check(_lib.moe_fp8_encode_range(first_bits & 0xFFFFFFFF, n, _p(q), _stream(stream)), "moe_fp8_encode_range")
+
+
+def moe_path_info(shp: MoeShape, M: int) -> tuple[int, str]:
+    buf = ctypes.create_string_buffer(1024)
+    st = _lib.moe_path_info(ctypes.byref(shp), M, buf, len(buf))
+    return st, buf.value.decode()
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def raw():
+    """The underlying ctypes library (for argument-validation tests)."""
+    return _lib

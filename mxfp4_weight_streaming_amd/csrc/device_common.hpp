@@ -1,0 +1,211 @@
+// device_common.hpp -- number formats and wave helpers shared by the gfx950 kernels.
+//
+// Formats (the pages name MXFP4 weights and FP8 activations but do not define
+// them; these follow the OCP MX v1.0 and OCP OFP8 definitions):
+//   E2M1  : decoded by the gfx950 scaled-conversion instruction
+//           (v_cvt_scalef32_pk_f16_fp4), two codes per byte, low nibble first.
+//   E8M0  : 2^(code-127), applied to fp32 block sums with v_ldexp_f32 (exact).
+//   E4M3  : OCP "FN" variant (bias 7, no infinity, max 448), encoded here with
+//           integer round-to-nearest-even and saturation to 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// E4M3 encode: nearest finite value, ties to the even code, |y| >= 448 -> 448,
+// sign kept (-0 -> 0x80); NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float y)
+{
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    uint32_t code;
+    if (a != a) {
+        return 0x7Fu;
+    } else if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {                  // below 2^-6: subnormal grid, step 2^-9
+        code = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, RNE; 8 means 2^-6
+    } else {                                     // normal: keep 3 mantissa bits, RNE
+        const uint32_t u = __float_as_uint(a);
+        const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+        code = r - (120u << 3);                  // rebias exponent 127 -> 7
+    }
+    return code | sign;
+}
+
+// E4M3 code -> fp32 value (exact).
+__device__ __forceinline__ float e4m3_decode(uint32_t c)
+{
+    const uint32_t em = c & 0x7Fu;
+    const float mag = (em >= 8u) ? __uint_as_float((em + (120u << 3)) << 20)
+                                 : (float)em * 0.001953125f;          // m * 2^-9
+    return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+}
+
+// Two fp32 values that are exact in f16 -> packed half2 bits.
+__device__ __forceinline__ uint32_t pack_half2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// 8 E4M3 codes (little-endian in a u32x2) -> 8 halves in a u32x4 (exact).
+__device__ __forceinline__ u32x4 e4m3x8_to_half8(u32x2 c)
+{
+    u32x4 r;
+    r.x = pack_half2(e4m3_decode(c.x & 0xFFu), e4m3_decode((c.x >> 8) & 0xFFu));
+    r.y = pack_half2(e4m3_decode((c.x >> 16) & 0xFFu), e4m3_decode(c.x >> 24));
+    r.z = pack_half2(e4m3_decode(c.y & 0xFFu), e4m3_decode((c.y >> 8) & 0xFFu));
+    r.w = pack_half2(e4m3_decode((c.y >> 16) & 0xFFu), e4m3_decode(c.y >> 24));
+    return r;
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// One dword of 8 E2M1 codes -> 4 half2 (true values, elements 2b and 2b+1 of byte b).
+__device__ __forceinline__ void e2m1x8_to_half(uint32_t d, half2_t* o)
+{
+    o[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
+    o[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
+    o[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
+    o[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
+}
+
+// Dot product of one 32-element MXFP4 block (16 bytes of codes, decoded) with
+// 32 f16 activations held as four u32x4 (8 halves each), in fp32.  Two
+// accumulators shorten the dependent chain.
+__device__ __forceinline__ float block_dot(const half2_t* w, u32x4 a0, u32x4 a1, u32x4 a2, u32x4 a3)
+{
+    float s0 = 0.0f, s1 = 0.0f;
+    s0 = __builtin_amdgcn_fdot2(w[0], as_half2(a0.x), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[1], as_half2(a0.y), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[2], as_half2(a0.z), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[3], as_half2(a0.w), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[4], as_half2(a1.x), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[5], as_half2(a1.y), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[6], as_half2(a1.z), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[7], as_half2(a1.w), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[8], as_half2(a2.x), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[9], as_half2(a2.y), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[10], as_half2(a2.z), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[11], as_half2(a2.w), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[12], as_half2(a3.x), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[13], as_half2(a3.y), s1, false);
+    s0 = __builtin_amdgcn_fdot2(w[14], as_half2(a3.z), s0, false);
+    s1 = __builtin_amdgcn_fdot2(w[15], as_half2(a3.w), s1, false);
+    return s0 + s1;
+}
+
+__device__ __forceinline__ float ldexp_e8m0(float v, uint32_t code)
+{
+    return __builtin_amdgcn_ldexpf(v, (int)code - 127);
+}
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p)
+{
+    return __builtin_nontemporal_load(p);   // weights are read once per call
+}
+
+// Cross-lane helpers on DPP (no LDS round trip): four steps reduce each row of
+// 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
+// results are read as scalars and combined in a fixed order, so every lane
+// gets the same, deterministic result.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float row_lane(float v, int lane)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16); every lane of a
+// group gets the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+    if constexpr (N >= 2) v += dpp_f32<kDppXor1>(v);
+    if constexpr (N >= 4) v += dpp_f32<kDppXor2>(v);
+    if constexpr (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_f32<kDppMirror>(v);
+    return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+
+__device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wave-wide maximum of an unsigned 32-bit value (uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Wave-wide maximum of a 64-bit key; the result is uniform across the wave.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    v = max_u64(v, dpp_u64<kDppXor1>(v));
+    v = max_u64(v, dpp_u64<kDppXor2>(v));
+    v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kDppMirror>(v));
+    return max_u64(max_u64(read_lane_u64(v, 0), read_lane_u64(v, 16)),
+                   max_u64(read_lane_u64(v, 32), read_lane_u64(v, 48)));
+}
+
+}  // namespace moe

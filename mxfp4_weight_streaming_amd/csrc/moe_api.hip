@@ -1,0 +1,347 @@
+// moe_api.hip -- the C ABI declared in include/moe_decode.h: argument
+// validation, workspace carving and launch ordering on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_decode.h"
+#include "moe_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status hip_fail(hipError_t err, const char* what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int token_bound(int M)
+{
+    int mt = 1;
+    while (mt < M) mt <<= 1;
+    return mt;
+}
+
+// Shape checks shared by every entry point.
+moe_status check_shape(const moe_shape* s, int32_t M)
+{
+    if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (s->hidden <= 0 || s->inter <= 0 || s->num_experts <= 0 || s->topk <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "shape has a non-positive size (H=%d I=%d E=%d K=%d)",
+                    s->hidden, s->inter, s->num_experts, s->topk);
+    if (s->hidden % 32 != 0 || s->inter % 32 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "H (%d) and I (%d) must be multiples of the MX block size 32",
+                    s->hidden, s->inter);
+    if (s->topk > s->num_experts)
+        return fail(MOE_ERR_INVALID_ARG, "K (%d) exceeds E (%d)", s->topk, s->num_experts);
+    if (M <= 0) return fail(MOE_ERR_INVALID_ARG, "M (%d) must be positive", M);
+    if (s->topk > moe::kMaxTopK)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K (%d) above %d is not compiled", s->topk, moe::kMaxTopK);
+    if (s->num_experts > moe::kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E (%d) above %d is not compiled", s->num_experts, moe::kMaxExperts);
+    if (!moe::gemv_shape_supported(s->hidden, s->inter))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "(H=%d, I=%d) is not a compiled shape; compiled: (256,64), (2560,768)",
+                    s->hidden, s->inter);
+    if (M > moe::kMaxGemvTokens)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "M=%d above %d tokens is not compiled", M, moe::kMaxGemvTokens);
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape* s, int32_t M, void* ws, size_t ws_bytes)
+{
+    if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t need = moe::ws_layout(s->hidden, s->inter, s->num_experts, s->topk, M).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for M=%d", ws_bytes, need, M);
+    return MOE_OK;
+}
+
+#define CHECK_PTR(p)                                                             \
+    do {                                                                         \
+        if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);  \
+    } while (0)
+#define CHECK_ALIGN(p)                                                                         \
+    do {                                                                                       \
+        if (!aligned16(p)) return fail(MOE_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p);    \
+    } while (0)
+
+struct Carved {
+    moe::WsLayout L;
+    char* base;
+    template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(base + off); }
+    moe::Compaction cp() const
+    {
+        return {at<int32_t>(L.n_act), at<int32_t>(L.act_experts), at<int32_t>(L.offsets),
+                at<int32_t>(L.pair_token), at<int32_t>(L.pair_src)};
+    }
+};
+
+Carved carve(const moe_shape* s, int32_t M, void* ws)
+{
+    return {moe::ws_layout(s->hidden, s->inter, s->num_experts, s->topk, M), static_cast<char*>(ws)};
+}
+
+int num_slots(const moe_shape* s, int32_t M)
+{
+    const int P = M * s->topk;
+    return s->num_experts < P ? s->num_experts : P;
+}
+
+moe_status enqueue_router(const moe_shape* s, int32_t M, const uint16_t* x, const uint16_t* wr, uint8_t* act_q,
+                          float* act_s, int32_t* ids_out, float* w_out, const Carved& c, hipStream_t st)
+{
+    moe::RouterArgs a{x, wr, M, s->num_experts, s->topk, c.at<float>(c.L.logits), act_q, act_s, ids_out, w_out,
+                      c.cp(), c.at<uint32_t>(c.L.counter)};
+    hipError_t e = moe::launch_router(s->hidden, token_bound(M), a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "router launch");
+}
+
+// Compaction of caller-given ids (one workgroup).
+moe_status enqueue_compact(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st)
+{
+    moe::TopkArgs a{{M, s->num_experts, s->topk, nullptr, ids}, nullptr, nullptr, c.cp()};
+    hipError_t e = moe::launch_topk(a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "compact launch");
+}
+
+moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
+                           const uint8_t* w13, const uint8_t* s13, float* h, const uint8_t* w2_prefetch,
+                           const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st)
+{
+    moe::GateUpArgs a{s->num_experts, M, s->topk, c.cp(), w13, s13, act_q, act_s, h, w2_prefetch, sw2_prefetch,
+                      nullptr};
+    hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
+}
+
+moe_status enqueue_requant(const moe_shape* s, int32_t M, const float* h, uint8_t* q2, float* s2, hipStream_t st)
+{
+    moe::RequantArgs a{h, M * s->topk, q2, s2};
+    hipError_t e = moe::launch_requant(s->inter, a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "requant launch");
+}
+
+moe_status enqueue_down(const moe_shape* s, int32_t M, const uint8_t* q2, const float* s2, const float* topk_w,
+                        const uint8_t* w2, const uint8_t* sw2, float* out, const Carved& c, hipStream_t st)
+{
+    moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, q2, s2, topk_w, c.cp(), out};
+    hipError_t e = moe::launch_down(s->hidden, s->inter, token_bound(M), a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
+}
+
+moe_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st)
+{
+    if (dst == nullptr || bytes == 0) return MOE_OK;
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "tap copy");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens)
+{
+    if (check_shape(shape, max_tokens) != MOE_OK) return 0;
+    return moe::ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->topk, max_tokens).total;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream)
+{
+    if (ws == nullptr || ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace is NULL or below 256 bytes");
+    if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    // the router's arrival counter must start at zero; zeroing the rest makes a
+    // never-written compaction read as "no active expert"
+    hipError_t e = moe::launch_fill_u32(static_cast<uint32_t*>(ws), ws_bytes / 4, 0u, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "workspace init");
+}
+
+moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const uint16_t* hidden,
+                                     const uint16_t* router_w, const uint8_t* w13, const uint8_t* w13_scale,
+                                     const uint8_t* w2, const uint8_t* w2_scale, float* out, void* ws,
+                                     size_t ws_bytes, void* stream, void* const* events)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(hidden); CHECK_PTR(router_w); CHECK_PTR(w13); CHECK_PTR(w13_scale);
+    CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(hidden); CHECK_ALIGN(router_w); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> moe_status {
+        if (events == nullptr || events[i] == nullptr) return MOE_OK;
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+    };
+    const Carved c = carve(shape, M, ws);
+    int32_t* ids = c.at<int32_t>(c.L.ids);
+    float* w = c.at<float>(c.L.w);
+    uint8_t* q = c.at<uint8_t>(c.L.act_q);
+    float* sc = c.at<float>(c.L.act_s);
+    float* h = c.at<float>(c.L.h);
+    uint8_t* q2 = c.at<uint8_t>(c.L.q2);
+    float* s2 = c.at<float>(c.L.s2);
+    if ((st = mark(0)) != MOE_OK) return st;
+    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, ids, w, c, s)) != MOE_OK) return st;
+    if ((st = mark(1)) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, q, sc, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK) return st;
+    if ((st = mark(2)) != MOE_OK) return st;
+    if ((st = enqueue_requant(shape, M, h, q2, s2, s)) != MOE_OK) return st;
+    if ((st = enqueue_down(shape, M, q2, s2, w, w2, w2_scale, out, c, s)) != MOE_OK) return st;
+    return mark(3);
+}
+
+moe_status moe_decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,
+                              const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2,
+                              const uint8_t* w2_scale, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    return moe_decode_forward_events(shape, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, ws_bytes,
+                                     stream, nullptr);
+}
+
+moe_status moe_route(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,
+                     int32_t* topk_ids, float* topk_w, const moe_route_taps* taps, void* ws, size_t ws_bytes,
+                     void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(hidden); CHECK_PTR(router_w); CHECK_PTR(topk_ids); CHECK_PTR(topk_w);
+    CHECK_ALIGN(hidden); CHECK_ALIGN(router_w);
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Carved c = carve(shape, M, ws);
+    uint8_t* act_q = taps ? taps->act_fp8 : nullptr;
+    float* act_s = taps ? taps->act_scale : nullptr;
+    if ((act_q == nullptr) != (act_s == nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "taps act_fp8 and act_scale must be given together");
+    if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, topk_ids, topk_w, c, s)) != MOE_OK)
+        return st;
+    if (taps == nullptr) return MOE_OK;
+    const size_t P = (size_t)M * shape->topk, S = (size_t)num_slots(shape, M);
+    if ((st = copy_out(taps->logits, c.at<void>(c.L.logits), (size_t)M * shape->num_experts * 4, s)) != MOE_OK) return st;
+    if ((st = copy_out(taps->n_active, c.at<void>(c.L.n_act), 4, s)) != MOE_OK) return st;
+    if ((st = copy_out(taps->act_experts, c.at<void>(c.L.act_experts), S * 4, s)) != MOE_OK) return st;
+    if ((st = copy_out(taps->offsets, c.at<void>(c.L.offsets), (S + 1) * 4, s)) != MOE_OK) return st;
+    if ((st = copy_out(taps->pair_token, c.at<void>(c.L.pair_token), P * 4, s)) != MOE_OK) return st;
+    return copy_out(taps->pair_src, c.at<void>(c.L.pair_src), P * 4, s);
+}
+
+moe_status moe_quant_act(const moe_shape* shape, int32_t M, const uint16_t* hidden, uint8_t* act_fp8,
+                         float* act_scale, void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(hidden); CHECK_PTR(act_fp8); CHECK_PTR(act_scale);
+    hipError_t e = moe::launch_quant(shape->hidden, hidden, M, act_fp8, act_scale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "quant launch");
+}
+
+moe_status moe_experts_forward(const moe_shape* shape, int32_t M, const uint8_t* act_fp8, const float* act_scale,
+                               const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                               const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
+                               const moe_expert_taps* taps, void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(act_fp8); CHECK_PTR(act_scale); CHECK_PTR(topk_ids); CHECK_PTR(topk_w);
+    CHECK_PTR(w13); CHECK_PTR(w13_scale); CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(act_fp8); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Carved c = carve(shape, M, ws);
+    float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
+    uint8_t* q2 = (taps && taps->inter_fp8) ? taps->inter_fp8 : c.at<uint8_t>(c.L.q2);
+    float* s2 = (taps && taps->inter_scale) ? taps->inter_scale : c.at<float>(c.L.s2);
+    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK)
+        return st;
+    if ((st = enqueue_requant(shape, M, h, q2, s2, s)) != MOE_OK) return st;
+    return enqueue_down(shape, M, q2, s2, topk_w, w2, w2_scale, out, c, s);
+}
+
+moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8, const float* act_scale,
+                       const int32_t* topk_ids, const uint8_t* w13, const uint8_t* w13_scale, float* h,
+                       uint8_t* inter_fp8, float* inter_scale, void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(act_fp8); CHECK_PTR(act_scale); CHECK_PTR(topk_ids); CHECK_PTR(w13); CHECK_PTR(w13_scale);
+    CHECK_PTR(h); CHECK_PTR(inter_fp8); CHECK_PTR(inter_scale);
+    CHECK_ALIGN(act_fp8); CHECK_ALIGN(w13);
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Carved c = carve(shape, M, ws);
+    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, h, nullptr, nullptr, c, s)) != MOE_OK)
+        return st;
+    return enqueue_requant(shape, M, h, inter_fp8, inter_scale, s);
+}
+
+moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* inter_fp8, const float* inter_scale,
+                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w2, const uint8_t* w2_scale,
+                            float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(inter_fp8); CHECK_PTR(inter_scale); CHECK_PTR(topk_ids); CHECK_PTR(topk_w);
+    CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(inter_fp8); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Carved c = carve(shape, M, ws);
+    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+    return enqueue_down(shape, M, inter_fp8, inter_scale, topk_w, w2, w2_scale, out, c, s);
+}
+
+moe_status moe_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* q, void* stream)
+{
+    if (q == nullptr) return fail(MOE_ERR_INVALID_ARG, "q is NULL");
+    if (n < 0) return fail(MOE_ERR_INVALID_ARG, "n (%lld) is negative", (long long)n);
+    hipError_t e = moe::launch_fp8_encode_range(first_bits, n, q, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fp8 encode launch");
+}
+
+moe_status moe_path_info(const moe_shape* shape, int32_t M, char* buf, size_t len)
+{
+    moe_status st = check_shape(shape, M);
+    if (buf != nullptr && len > 0) {
+        if (st != MOE_OK)
+            snprintf(buf, len, "unsupported: %s", g_last_error);
+        else
+            snprintf(buf, len, "gemv path, M=%d (token bound %d), E=%d, K=%d: %s", M, token_bound(M),
+                     shape->num_experts, shape->topk, moe::kernel_names(shape->hidden, shape->inter, token_bound(M)));
+    }
+    return st;
+}
+
+const char* moe_status_string(moe_status status)
+{
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// moe_internal.hpp -- kernel argument blocks, workspace layout and launcher
+// declarations shared by the kernels (moe_kernels.hip) and the C ABI
+// (moe_api.hip).  Not installed; the public interface is include/moe_decode.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Largest token count of the GEMV path, and largest K / E it supports.
+constexpr int kMaxGemvTokens = 8;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxPairs = kMaxGemvTokens * kMaxTopK;
+
+// Token -> expert compaction as published in the workspace.
+struct Compaction {
+    int32_t* n_act;        // [1]
+    int32_t* act_experts;  // [S] ascending expert ids
+    int32_t* offsets;      // [S+1]
+    int32_t* pair_token;   // [M*K]
+    int32_t* pair_src;     // [M*K] original pair index t*K+j
+};
+
+struct RouterArgs {
+    const uint16_t* x;     // [M,H] bf16
+    const uint16_t* wr;    // [E,H] bf16
+    int M, E, K;
+    float* logits;         // [M,E]
+    uint8_t* act_q;        // [M,H] or nullptr (no quantisation)
+    float* act_s;          // [M]
+    int32_t* ids_out;      // [M,K] routing published by the last workgroup
+    float* w_out;          // [M,K]
+    Compaction cp;         // published by the last workgroup
+    uint32_t* counter;     // arrival counter (the last workgroup resets it)
+};
+
+// Routing source of a prologue: logits (top-K computed in the workgroup) or
+// caller-given ids.
+struct RouteSrc {
+    int M, E, K;
+    const float* logits;   // [M,E] or nullptr
+    const int32_t* ids;    // [M,K] used when logits is nullptr
+};
+
+struct TopkArgs {
+    RouteSrc src;
+    int32_t* ids_out;      // [M,K]
+    float* w_out;          // [M,K] (only with logits)
+    Compaction cp;
+};
+
+struct GateUpArgs {
+    int E, M, K;
+    Compaction cp;         // read
+    const uint8_t* w13;    // [E,2I,H/2]
+    const uint8_t* s13;    // [E,2I,H/32]
+    const uint8_t* act_q;  // [M,H]
+    const float* act_s;    // [M]
+    float* h;              // [M*K,I]
+    const uint8_t* w2;     // [E,H,I/2] down weights to prefetch, or nullptr
+    const uint8_t* sw2;    // [E,H,I/32]
+    uint32_t* sink;        // never-null only to keep prefetch loads alive; pass nullptr
+};
+
+struct DownArgs {
+    int E, M, K;
+    const uint8_t* w2;     // [E,H,I/2]
+    const uint8_t* sw2;    // [E,H,I/32]
+    const uint8_t* q2;     // [M*K,I] E4M3 intermediate
+    const float* s2;       // [M*K]
+    const float* topk_w;   // [M*K]
+    Compaction cp;         // read
+    float* out;            // [M,H]
+};
+
+struct RequantArgs {
+    const float* h;        // [P,I]
+    int P;
+    uint8_t* q2;           // [P,I]
+    float* s2;             // [P]
+};
+
+// Workspace carving.  Only the control block at offset 0 (which does not
+// depend on M) carries state between calls; it returns to zero after every call.
+struct WsLayout {
+    size_t counter, logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(int H, int I, int E, int K, int M)
+{
+    WsLayout L{};
+    const size_t P = (size_t)M * K;
+    const size_t S = (size_t)(E < (int)P ? E : (int)P);
+    size_t off = 256;      // control block: the router's arrival counter
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    L.counter = 0;
+    L.logits = take((size_t)M * E * 4);
+    L.ids = take(P * 4);
+    L.w = take(P * 4);
+    L.act_q = take((size_t)M * H);
+    L.act_s = take((size_t)M * 4);
+    L.n_act = take(4);
+    L.act_experts = take(S * 4);
+    L.offsets = take((S + 1) * 4);
+    L.pair_token = take(P * 4);
+    L.pair_src = take(P * 4);
+    L.h = take(P * I * 4);
+    L.q2 = take(P * I);
+    L.s2 = take(P * 4);
+    L.total = off;
+    return L;
+}
+
+// Launchers (moe_kernels.hip).  Each returns the hipError_t of its launch.
+// mt is the token bound the kernels are instantiated for (1, 2, 4 or 8).
+bool gemv_shape_supported(int H, int I);
+hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s);
+hipError_t launch_quant(int H, const uint16_t* x, int M, uint8_t* q, float* sc, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s);
+hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
+hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+const char* kernel_names(int H, int I, int mt);
+
+}  // namespace moe
