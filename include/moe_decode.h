@@ -121,9 +121,9 @@ typedef struct {
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens);
 
 /* Zero the workspace (a fill kernel on `stream`; the caller orders later
- * calls on other streams after it).  Call once after allocating a workspace;
- * later calls keep its control block clean themselves.  ws must be 256-byte
- * aligned. */
+ * calls on other streams after it).  No call depends on what an earlier call
+ * left in the workspace, so this is optional; it makes a workspace that was
+ * never written read as "no expert selected".  ws must be 256-byte aligned. */
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* The whole layer for M tokens: route -> quantise -> compact -> gate/up ->
@@ -136,8 +136,7 @@ moe_status moe_decode_forward(const moe_shape* shape, int32_t M,
 
 /* moe_decode_forward that also records caller-created HIP events on `stream`
  * for per-kernel timing: events[0] before the router kernel, events[1] after
- * it, events[2] after the gate/up kernel, events[3] after the requantisation
- * and down kernels.
+ * it, events[2] after the gate/up kernel, events[3] after the down kernel.
  * `events` (an array of 4 hipEvent_t) or any element may be NULL.  Usable
  * under stream capture (the records become graph event nodes). */
 moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M,
@@ -163,7 +162,8 @@ moe_status moe_quant_act(const moe_shape* shape, int32_t M, const uint16_t* hidd
 
 /* Everything after routing, on caller-given routing (e.g. an oracle's ids and
  * weights for tokens whose K-th and (K+1)-th logits are too close to call):
- * compaction -> gate/up -> requantise -> down + combine.  taps may be NULL. */
+ * compaction -> gate/up -> requantise -> down + combine, with the same
+ * kernels as moe_decode_forward.  taps may be NULL. */
 moe_status moe_experts_forward(const moe_shape* shape, int32_t M,
                                const uint8_t* act_fp8, const float* act_scale,
                                const int32_t* topk_ids, const float* topk_w,
@@ -172,8 +172,10 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M,
                                float* out, const moe_expert_taps* taps,
                                void* ws, size_t ws_bytes, void* stream);
 
-/* Compaction and the fused gate/up kernel alone: writes h, the E4M3
- * intermediate and its scales.  All three outputs are required. */
+/* Compaction and the fused gate/up kernel, then the per-(token, expert) FP8
+ * requantisation as a kernel of its own (moe_decode_forward does the same
+ * arithmetic inside its down kernel): writes h, the E4M3 intermediate and its
+ * scales.  All three outputs are required. */
 moe_status moe_gate_up(const moe_shape* shape, int32_t M,
                        const uint8_t* act_fp8, const float* act_scale,
                        const int32_t* topk_ids,

@@ -22,25 +22,46 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// E4M3 encode: nearest finite value, ties to the even code, |y| >= 448 -> 448,
-// sign kept (-0 -> 0x80); NaN -> 0x7F.
+// E4M3 encode: nearest finite value, ties to the even code, |y| > 448 -> 448,
+// sign kept (-0 -> 0x80); NaN -> 0x7F.  gfx950's v_cvt_pk_fp8_f32 converts to
+// OCP E4M3 with round-to-nearest-even; clamping to +-448 first (v_med3) gives
+// the saturating behaviour.
 __device__ __forceinline__ uint32_t e4m3_encode(float y)
 {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
-    uint32_t code;
-    if (a != a) {
-        return 0x7Fu;
-    } else if (a >= 448.0f) {
-        code = 0x7Eu;
-    } else if (a < 0.015625f) {                  // below 2^-6: subnormal grid, step 2^-9
-        code = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, RNE; 8 means 2^-6
-    } else {                                     // normal: keep 3 mantissa bits, RNE
-        const uint32_t u = __float_as_uint(a);
-        const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
-        code = r - (120u << 3);                  // rebias exponent 127 -> 7
-    }
-    return code | sign;
+    if (y != y) return 0x7Fu;
+    const float c = __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// Four values -> four E4M3 codes in one dword (byte i = value i), same
+// rounding and saturation (NaN inputs are not expected here).
+__device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Two E4M3 codes (bytes 0,1 when HI is false, 2,3 when true) -> their exact
+// values as half2.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_half2(uint32_t codes)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, 1.0f, HI));
+}
+
+// 8 E4M3 codes (little-endian in a u32x2) -> 8 halves in a u32x4 (exact).
+__device__ __forceinline__ u32x4 e4m3x8_to_half8(u32x2 c)
+{
+    u32x4 r;
+    r.x = e4m3x2_to_half2<false>(c.x);
+    r.y = e4m3x2_to_half2<true>(c.x);
+    r.z = e4m3x2_to_half2<false>(c.y);
+    r.w = e4m3x2_to_half2<true>(c.y);
+    return r;
 }
 
 // E4M3 code -> fp32 value (exact).
@@ -50,23 +71,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c)
     const float mag = (em >= 8u) ? __uint_as_float((em + (120u << 3)) << 20)
                                  : (float)em * 0.001953125f;          // m * 2^-9
     return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
-}
-
-// Two fp32 values that are exact in f16 -> packed half2 bits.
-__device__ __forceinline__ uint32_t pack_half2(float a, float b)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// 8 E4M3 codes (little-endian in a u32x2) -> 8 halves in a u32x4 (exact).
-__device__ __forceinline__ u32x4 e4m3x8_to_half8(u32x2 c)
-{
-    u32x4 r;
-    r.x = pack_half2(e4m3_decode(c.x & 0xFFu), e4m3_decode((c.x >> 8) & 0xFFu));
-    r.y = pack_half2(e4m3_decode((c.x >> 16) & 0xFFu), e4m3_decode(c.x >> 24));
-    r.z = pack_half2(e4m3_decode(c.y & 0xFFu), e4m3_decode((c.y >> 8) & 0xFFu));
-    r.w = pack_half2(e4m3_decode((c.y >> 16) & 0xFFu), e4m3_decode(c.y >> 24));
-    return r;
 }
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }

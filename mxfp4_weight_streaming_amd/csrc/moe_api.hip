@@ -103,28 +103,32 @@ int num_slots(const moe_shape* s, int32_t M)
 }
 
 moe_status enqueue_router(const moe_shape* s, int32_t M, const uint16_t* x, const uint16_t* wr, uint8_t* act_q,
-                          float* act_s, int32_t* ids_out, float* w_out, const Carved& c, hipStream_t st)
+                          float* act_s, const Carved& c, hipStream_t st)
 {
-    moe::RouterArgs a{x, wr, M, s->num_experts, s->topk, c.at<float>(c.L.logits), act_q, act_s, ids_out, w_out,
-                      c.cp(), c.at<uint32_t>(c.L.counter)};
+    moe::RouterArgs a{x, wr, M, s->num_experts, c.at<float>(c.L.logits), act_q, act_s};
     hipError_t e = moe::launch_router(s->hidden, token_bound(M), a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "router launch");
 }
 
-// Compaction of caller-given ids (one workgroup).
-moe_status enqueue_compact(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st)
+// Top-K and compaction in one workgroup, from the logits in the workspace or
+// from caller-given ids.
+moe_status enqueue_topk(const moe_shape* s, int32_t M, bool from_logits, const int32_t* ids, int32_t* ids_out,
+                        float* w_out, const Carved& c, hipStream_t st)
 {
-    moe::TopkArgs a{{M, s->num_experts, s->topk, nullptr, ids}, nullptr, nullptr, c.cp()};
+    moe::TopkArgs a{{M, s->num_experts, s->topk, from_logits ? c.at<float>(c.L.logits) : nullptr, ids}, ids_out,
+                    w_out, c.cp()};
     hipError_t e = moe::launch_topk(a, st);
-    return e == hipSuccess ? MOE_OK : hip_fail(e, "compact launch");
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "topk launch");
 }
 
-moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
-                           const uint8_t* w13, const uint8_t* s13, float* h, const uint8_t* w2_prefetch,
-                           const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st)
+// The gate/up kernel routes from the workspace logits (ids == nullptr) or
+// from caller-given ids.
+moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const int32_t* ids, int32_t* ids_out, float* w_out,
+                           const uint8_t* act_q, const float* act_s, const uint8_t* w13, const uint8_t* s13, float* h,
+                           const uint8_t* w2_prefetch, const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st)
 {
-    moe::GateUpArgs a{s->num_experts, M, s->topk, c.cp(), w13, s13, act_q, act_s, h, w2_prefetch, sw2_prefetch,
-                      nullptr};
+    const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids};
+    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, w2_prefetch, sw2_prefetch, nullptr};
     hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
 }
@@ -136,10 +140,13 @@ moe_status enqueue_requant(const moe_shape* s, int32_t M, const float* h, uint8_
     return e == hipSuccess ? MOE_OK : hip_fail(e, "requant launch");
 }
 
-moe_status enqueue_down(const moe_shape* s, int32_t M, const uint8_t* q2, const float* s2, const float* topk_w,
-                        const uint8_t* w2, const uint8_t* sw2, float* out, const Carved& c, hipStream_t st)
+// From h (requantised in the kernel; q2_out/s2_out optional taps) or from a
+// caller's E4M3 intermediate q2/s2.
+moe_status enqueue_down(const moe_shape* s, int32_t M, const float* h, const uint8_t* q2, const float* s2,
+                        uint8_t* q2_out, float* s2_out, const float* topk_w, const uint8_t* w2, const uint8_t* sw2,
+                        float* out, const Carved& c, hipStream_t st)
 {
-    moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, q2, s2, topk_w, c.cp(), out};
+    moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, h, q2, s2, q2_out, s2_out, topk_w, c.cp(), out};
     hipError_t e = moe::launch_down(s->hidden, s->inter, token_bound(M), a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
 }
@@ -165,8 +172,8 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream)
 {
     if (ws == nullptr || ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace is NULL or below 256 bytes");
     if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    // the router's arrival counter must start at zero; zeroing the rest makes a
-    // never-written compaction read as "no active expert"
+    // no call reads what an earlier call left; zeroing makes a never-written
+    // compaction read as "no active expert"
     hipError_t e = moe::launch_fill_u32(static_cast<uint32_t*>(ws), ws_bytes / 4, 0u, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "workspace init");
 }
@@ -194,15 +201,14 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
     uint8_t* q = c.at<uint8_t>(c.L.act_q);
     float* sc = c.at<float>(c.L.act_s);
     float* h = c.at<float>(c.L.h);
-    uint8_t* q2 = c.at<uint8_t>(c.L.q2);
-    float* s2 = c.at<float>(c.L.s2);
     if ((st = mark(0)) != MOE_OK) return st;
-    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, ids, w, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s)) != MOE_OK) return st;
     if ((st = mark(1)) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, q, sc, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK)
+        return st;
     if ((st = mark(2)) != MOE_OK) return st;
-    if ((st = enqueue_requant(shape, M, h, q2, s2, s)) != MOE_OK) return st;
-    if ((st = enqueue_down(shape, M, q2, s2, w, w2, w2_scale, out, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s)) != MOE_OK)
+        return st;
     return mark(3);
 }
 
@@ -229,8 +235,8 @@ moe_status moe_route(const moe_shape* shape, int32_t M, const uint16_t* hidden, 
     float* act_s = taps ? taps->act_scale : nullptr;
     if ((act_q == nullptr) != (act_s == nullptr))
         return fail(MOE_ERR_INVALID_ARG, "taps act_fp8 and act_scale must be given together");
-    if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, topk_ids, topk_w, c, s)) != MOE_OK)
-        return st;
+    if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, c, s)) != MOE_OK) return st;
+    if ((st = enqueue_topk(shape, M, true, nullptr, topk_ids, topk_w, c, s)) != MOE_OK) return st;
     if (taps == nullptr) return MOE_OK;
     const size_t P = (size_t)M * shape->topk, S = (size_t)num_slots(shape, M);
     if ((st = copy_out(taps->logits, c.at<void>(c.L.logits), (size_t)M * shape->num_experts * 4, s)) != MOE_OK) return st;
@@ -265,13 +271,12 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M, const uint8_t*
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
     float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
-    uint8_t* q2 = (taps && taps->inter_fp8) ? taps->inter_fp8 : c.at<uint8_t>(c.L.q2);
-    float* s2 = (taps && taps->inter_scale) ? taps->inter_scale : c.at<float>(c.L.s2);
-    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK)
+    uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
+    float* s2_tap = taps ? taps->inter_scale : nullptr;
+    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, w2,
+                              w2_scale, c, s)) != MOE_OK)
         return st;
-    if ((st = enqueue_requant(shape, M, h, q2, s2, s)) != MOE_OK) return st;
-    return enqueue_down(shape, M, q2, s2, topk_w, w2, w2_scale, out, c, s);
+    return enqueue_down(shape, M, h, nullptr, nullptr, q2_tap, s2_tap, topk_w, w2, w2_scale, out, c, s);
 }
 
 moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8, const float* act_scale,
@@ -286,8 +291,8 @@ moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
-    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, h, nullptr, nullptr, c, s)) != MOE_OK)
+    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, nullptr,
+                              nullptr, c, s)) != MOE_OK)
         return st;
     return enqueue_requant(shape, M, h, inter_fp8, inter_scale, s);
 }
@@ -304,8 +309,8 @@ moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* in
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
-    if ((st = enqueue_compact(shape, M, topk_ids, c, s)) != MOE_OK) return st;
-    return enqueue_down(shape, M, inter_fp8, inter_scale, topk_w, w2, w2_scale, out, c, s);
+    if ((st = enqueue_topk(shape, M, false, topk_ids, nullptr, nullptr, c, s)) != MOE_OK) return st;
+    return enqueue_down(shape, M, nullptr, inter_fp8, inter_scale, nullptr, nullptr, topk_w, w2, w2_scale, out, c, s);
 }
 
 moe_status moe_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* q, void* stream)

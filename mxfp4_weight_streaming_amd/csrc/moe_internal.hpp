@@ -27,14 +27,10 @@ struct Compaction {
 struct RouterArgs {
     const uint16_t* x;     // [M,H] bf16
     const uint16_t* wr;    // [E,H] bf16
-    int M, E, K;
+    int M, E;
     float* logits;         // [M,E]
     uint8_t* act_q;        // [M,H] or nullptr (no quantisation)
     float* act_s;          // [M]
-    int32_t* ids_out;      // [M,K] routing published by the last workgroup
-    float* w_out;          // [M,K]
-    Compaction cp;         // published by the last workgroup
-    uint32_t* counter;     // arrival counter (the last workgroup resets it)
 };
 
 // Routing source of a prologue: logits (top-K computed in the workgroup) or
@@ -53,8 +49,10 @@ struct TopkArgs {
 };
 
 struct GateUpArgs {
-    int E, M, K;
-    Compaction cp;         // read
+    RouteSrc src;          // logits (top-K in every workgroup) or caller ids
+    int32_t* ids_out;      // [M,K] published by workgroup 0; may be nullptr
+    float* w_out;          // [M,K]; may be nullptr
+    Compaction cp;         // published by workgroup 0
     const uint8_t* w13;    // [E,2I,H/2]
     const uint8_t* s13;    // [E,2I,H/32]
     const uint8_t* act_q;  // [M,H]
@@ -69,8 +67,11 @@ struct DownArgs {
     int E, M, K;
     const uint8_t* w2;     // [E,H,I/2]
     const uint8_t* sw2;    // [E,H,I/32]
-    const uint8_t* q2;     // [M*K,I] E4M3 intermediate
+    const float* h;        // [M*K,I] fp32, requantised in the kernel; or nullptr
+    const uint8_t* q2;     // [M*K,I] E4M3 intermediate, used when h is nullptr
     const float* s2;       // [M*K]
+    uint8_t* q2_out;       // optional: the requantised codes (workgroup 0 writes them)
+    float* s2_out;         // optional: their scales
     const float* topk_w;   // [M*K]
     Compaction cp;         // read
     float* out;            // [M,H]
@@ -83,10 +84,10 @@ struct RequantArgs {
     float* s2;             // [P]
 };
 
-// Workspace carving.  Only the control block at offset 0 (which does not
-// depend on M) carries state between calls; it returns to zero after every call.
+// Workspace carving.  No state is carried between calls: every call writes
+// what it later reads.
 struct WsLayout {
-    size_t counter, logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, total;
+    size_t logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -96,9 +97,8 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     WsLayout L{};
     const size_t P = (size_t)M * K;
     const size_t S = (size_t)(E < (int)P ? E : (int)P);
-    size_t off = 256;      // control block: the router's arrival counter
+    size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    L.counter = 0;
     L.logits = take((size_t)M * E * 4);
     L.ids = take(P * 4);
     L.w = take(P * 4);
@@ -122,7 +122,7 @@ bool gemv_shape_supported(int H, int I);
 hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s);
 hipError_t launch_quant(int H, const uint16_t* x, int M, uint8_t* q, float* sc, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s);  // S: slot bound
 hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s);
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);

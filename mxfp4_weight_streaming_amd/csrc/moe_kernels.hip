@@ -3,25 +3,25 @@
 // The pages find batch-1 MoE decode bound by reading expert weights ([EN]
 // "Why is MoE decoding on DGX Spark memory-bound?"), so the kernels are built
 // around streaming MXFP4 bytes from HBM once, with wide loads issued before
-// any dependent work.  A layer is four kernels on one stream:
+// any dependent work.  A layer is three kernels on one stream:
 //   router_kernel   fp32 router GEMV (one wave per expert row) and per-token
-//                   FP8 quantisation of the activations; the last workgroup to
-//                   finish derives the routing once: top-K, renormalised
-//                   weights and the token->expert compaction ([EN] "What is
-//                   Ling 3.0...": 8 routed experts per token; [EN] "What are
-//                   the 3 optimizations?", item 3: a 4-token verify touches up
-//                   to 32 experts).
-//   gate_up_kernel  the fused gate/up MXFP4 GEMV of one selected expert's rows
-//                   with the SiLU(gate)*up epilogue ([EN] same section, item 1:
-//                   the 768-wide expert layer); it also pulls its expert's
+//                   FP8 quantisation of the activations.
+//   gate_up_kernel  every workgroup derives the routing from the logits
+//                   (top-K, renormalised weights, token->expert compaction:
+//                   [EN] "What is Ling 3.0...", 8 routed experts per token;
+//                   [EN] "What are the 3 optimizations?", item 3: a 4-token
+//                   verify touches up to 32 experts), then streams the fused
+//                   gate/up MXFP4 GEMV of (expert, row block) items with the
+//                   SiLU(gate)*up epilogue ([EN] same section, item 1: the
+//                   768-wide expert layer), pulling each expert's
 //                   down-projection weights into the memory-side cache.
-//   requant_kernel  per-(token, expert) FP8 requantisation of the intermediate.
-//   down_kernel     the down GEMV over all selected experts and the
-//                   router-weighted combine, in a fixed order (no float atomics).
-// Cross-workgroup synchronisation inside a kernel is used once per layer (the
-// router's last-arrival step, 64 workgroups): on this chip every device-scope
-// release costs a serialised L2 write-back, so kernel boundaries carry the
-// other dependencies.
+//   down_kernel     requantises the intermediate to FP8 per (token, expert)
+//                   row while its weight loads are in flight, then the down
+//                   GEMV over all selected experts and the router-weighted
+//                   combine in a fixed order (no float atomics).
+// Workgroups never synchronise with each other inside a kernel: on this chip
+// a device-scope release costs every workgroup a serialised L2 write-back,
+// far dearer than repeating a little work in every workgroup.
 // The M <= 8 path is a GEMV: it uses the vector ALU (dot2 on exactly decoded
 // f16 operands, fp32 accumulation), not the matrix cores.
 //   [EN] = "NVIDIA Shows 3 Ways to Speed Up MoE Inference on DGX Spark,
@@ -83,59 +83,117 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e)
     return ((uint64_t)f32_orderable(v + 0.0f) << 32) | (uint32_t)(~(uint32_t)e);   // + 0.0f folds -0 into +0
 }
 
-// Keys are unique, so each round's maximum belongs to exactly one lane.  Every
-// lane sorts its (at most 8) keys once; a round then compares only the lanes'
-// heads: first on the 32-bit orderable logit alone (one DPP max chain), and
-// only if several lanes share that logit exactly, on the full key, whose low
-// half makes the lower expert index win.
-__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out)
+// Per-wave LDS scratch of the top-K: the selected keys in ascending expert order.
+struct TopkScratch {
+    uint32_t u[kMaxTopK];
+    int32_t e[kMaxTopK];
+};
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Top-K of one token's E logits by one wave, as a radix select: 32 steps of
+// ballot counting find T, the K-th largest orderable logit; the selection is
+// every logit above T plus, among those equal to T, the lowest expert
+// indices.  The K winners are then ranked by (logit descending, index
+// ascending) and their weights are the softmax over the selected logits.
+template <int PER>
+__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out, TopkScratch& sc)
 {
     const int lane = threadIdx.x & 63;
-    constexpr int PER = kMaxExperts / kWave;
-    uint64_t k[PER];
+    uint32_t u[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {             // unconditional loads: all in flight together
+        const int e = lane + kWave * i;
+        const float v = L[e < E ? e : E - 1];
+        u[i] = (e < E) ? f32_orderable(v + 0.0f) : 0u;   // + 0.0f folds -0 into +0
+    }
+    // Radix select of T, the largest value with count(u >= T) >= K.  As soon
+    // as some candidate has exactly K keys at or above it, those K keys are
+    // the selection (every other key is strictly smaller) and the search stops.
+    uint32_t T = 0;
+    bool exact = false;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(u[i] >= cand));
+        if (cnt >= K) {
+            T = cand;
+            if (cnt == K) {
+                exact = true;
+                break;
+            }
+        }
+    }
+    uint64_t sel[PER];
+    if (exact) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sel[i] = __ballot(u[i] >= T);
+    } else {
+        // T is the K-th largest value: every key above T, then keys equal to T
+        // in ascending expert order (expert = lane + 64 * slot: slot-major)
+        int need = K;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            sel[i] = __ballot(u[i] > T);
+            need -= __popcll(sel[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            uint64_t m = __ballot(u[i] == T);
+            while (need > 0 && m != 0ull) {
+                const uint64_t low = m & (~m + 1ull);
+                sel[i] |= low;
+                m ^= low;
+                --need;
+            }
+        }
+    }
+    int base = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = lane + kWave * i;
-        k[i] = (e < E) ? topk_key(L[e], e) : 0ull;
-    }
-#pragma unroll
-    for (int i = 1; i < PER; ++i)            // insertion sort, descending
-#pragma unroll
-        for (int j = i; j > 0; --j) {
-            const uint64_t hi = max_u64(k[j - 1], k[j]), lo = k[j - 1] ^ k[j] ^ hi;
-            k[j - 1] = hi;
-            k[j] = lo;
+        if ((sel[i] >> lane) & 1ull) {
+            const int pos = base + __popcll(sel[i] & ((1ull << lane) - 1ull));
+            sc.u[pos] = u[i];
+            sc.e[pos] = lane + kWave * i;
         }
-    uint64_t mine = 0, first = 0;            // lane j keeps the j-th selected key
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < K) {
-            const uint32_t hi = (uint32_t)(k[0] >> 32);
-            const uint32_t best_hi = wave_max_u32(hi);
-            const uint64_t tied = __ballot(hi == best_hi);
-            uint64_t best;
-            if (__popcll(tied) == 1) {
-                const int owner = __ffsll((unsigned long long)tied) - 1;
-                best = ((uint64_t)best_hi << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k[0], owner);
-            } else {
-                best = wave_max_u64(hi == best_hi ? k[0] : 0ull);
-            }
-            if (j == 0) first = best;
-            if (lane == j) mine = best;
-            if (k[0] == best) {
-#pragma unroll
-                for (int i = 0; i + 1 < PER; ++i) k[i] = k[i + 1];
-                k[PER - 1] = 0ull;
-            }
-        }
+        base += __popcll(sel[i]);
     }
-    const float top = f32_from_orderable((uint32_t)(first >> 32));
-    const float ex = (lane < K) ? expf(f32_from_orderable((uint32_t)(mine >> 32)) - top) : 0.0f;
+    wave_lds_sync();
+    // every lane reads all kMaxTopK scratch entries (broadcast, unconditional);
+    // entries at or past K are masked out of the arithmetic
+    const uint32_t uj = sc.u[lane & (kMaxTopK - 1)];
+    const int ej = sc.e[lane & (kMaxTopK - 1)];
+    uint32_t umax = 0;
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        const uint32_t uk = sc.u[k];
+        const int ek = sc.e[k];
+        const bool in = k < K;
+        rank += in && ((uk > uj) || (uk == uj && ek < ej));
+        umax = in ? max(umax, uk) : umax;
+    }
+    const float ex = (lane < K) ? expf(f32_from_orderable(uj) - f32_from_orderable(umax)) : 0.0f;
     const float den = wave_sum(ex);
     if (lane < K) {
-        ids_out[lane] = (int32_t)(~(uint32_t)mine);
-        w_out[lane] = ex / den;
+        ids_out[rank] = ej;
+        w_out[rank] = ex / den;
     }
+    wave_lds_sync();   // the scratch may be reused by this wave's next token
+}
+
+__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out, TopkScratch& sc)
+{
+    if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out, sc);
+    else if (E <= 128) topk_wave_t<2>(L, E, K, ids_out, w_out, sc);
+    else if (E <= 256) topk_wave_t<4>(L, E, K, ids_out, w_out, sc);
+    else topk_wave_t<8>(L, E, K, ids_out, w_out, sc);
 }
 
 // ---------------------------------------------------------------------------
@@ -151,53 +209,68 @@ struct alignas(16) RouteLds {
     int32_t offsets[kMaxPairs + 1];
     int32_t pair_token[kMaxPairs];
     int32_t pair_src[kMaxPairs];
+    TopkScratch topk[4];
 };
 
-// One wave; lane p < P owns pair p.  Its compacted position is the number of
-// pairs ahead of it in (expert, pair index) order, counted from LDS broadcast
-// reads of the ids; a slot starts at every position whose pair is its
-// expert's first, and slot numbers come from a ballot prefix count.
-__device__ void compact_wave(int P, int K, RouteLds& r)
+// One wave; lane p < P owns pair p with expert e_p.  Its compacted position
+// is the number of pairs ahead of it in (expert, pair index) order; a pair
+// that is its expert's first gets slot = number of distinct smaller experts.
+// The ids (at most PMAX) are read once with broadcast LDS loads.
+template <int PMAX>
+__device__ void compact_wave_t(int P, int K, RouteLds& r)
 {
     const int lane = threadIdx.x & 63;
+    constexpr int NV = (PMAX + 3) / 4;
+    int4 ids4[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)       // unconditional: entries past P are ignored below
+        ids4[v] = *reinterpret_cast<const int4*>(r.ids + 4 * v);
     const int e = (lane < P) ? r.ids[lane] : 0;
     int pos = 0, same_before = 0;
-    for (int q0 = 0; q0 < P; q0 += 4) {      // reads stay inside the 64-entry array
-        const int4 v = *reinterpret_cast<const int4*>(r.ids + q0);
-        const int eq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int q = q0 + u;
-            if (q < P) {
-                pos += (eq[u] < e) || (eq[u] == e && q < lane);
-                same_before += (eq[u] == e) && (q < lane);
-            }
+            const int q = 4 * v + u;
+            const bool in = q < P;
+            pos += in && ((eq[u] < e) || (eq[u] == e && q < lane));
+            same_before += in && (eq[u] == e) && (q < lane);
         }
     }
-    // scratch: by position, the expert and whether it starts a slot
+    const bool first = lane < P && same_before == 0;
+    const uint64_t firsts = __ballot(first);
+    int slot = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = 4 * v + u;
+            slot += (q < P) && ((firsts >> q) & 1ull) && eq[u] < e;
+        }
+    }
     if (lane < P) {
         r.pair_token[pos] = lane / K;
         r.pair_src[pos] = lane;
-        r.act_experts[pos] = (same_before == 0) ? e : -1;   // temporary, compacted below
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const int pe = (lane < P) ? r.act_experts[lane] : -1;
-    const uint64_t starts = __ballot(pe >= 0);
-    const int slot = __popcll(starts & ((1ull << lane) - 1ull));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (pe >= 0) {
-        r.act_experts[slot] = pe;
-        r.offsets[slot] = lane;
+        if (first) {
+            r.act_experts[slot] = e;
+            r.offsets[slot] = pos;
+        }
     }
     if (lane == 0) {
-        const int n = __popcll(starts);
+        const int n = __popcll(firsts);
         r.n_act = n;
         r.offsets[n] = P;
     }
+}
+
+__device__ void compact_wave(int P, int K, RouteLds& r)
+{
+    if (P <= 8) compact_wave_t<8>(P, K, r);
+    else if (P <= 16) compact_wave_t<16>(P, K, r);
+    else if (P <= 32) compact_wave_t<32>(P, K, r);
+    else compact_wave_t<64>(P, K, r);
 }
 
 __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
@@ -205,12 +278,37 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
     const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
     const int M = src.M, E = src.E, K = src.K, P = M * K;
     if (src.logits != nullptr) {
-        for (int t = wave; t < M; t += nw) topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K);
+        for (int t = wave; t < M; t += nw)
+            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K, r.topk[wave]);
     } else {
         for (int i = tid; i < P; i += blockDim.x) r.ids[i] = min(max(src.ids[i], 0), E - 1);   // clamped, never OOB
     }
     __syncthreads();
-    if (wave == 0) compact_wave(P, K, r);
+    if (wave == 0) {
+        if (M == 1) {
+            // one token: its K experts are distinct, so the slots are the
+            // experts in ascending id and slot s holds exactly one pair
+            const int lane = tid & 63;
+            const int4 a4 = *reinterpret_cast<const int4*>(r.ids), b4 = *reinterpret_cast<const int4*>(r.ids + 4);
+            const int all[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+            const int e = r.ids[lane & (kMaxTopK - 1)];
+            int slot = 0;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) slot += (k < K) && all[k] < e;
+            if (lane < K) {
+                r.act_experts[slot] = e;
+                r.offsets[slot] = slot;
+                r.pair_token[slot] = 0;
+                r.pair_src[slot] = lane;
+            }
+            if (lane == 0) {
+                r.n_act = K;
+                r.offsets[K] = K;
+            }
+        } else {
+            compact_wave(P, K, r);
+        }
+    }
     __syncthreads();
 }
 
@@ -240,7 +338,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a)
 // ---------------------------------------------------------------------------
 // Router: logits[t,e] = x[t] . Wr[e] in fp32 (exact bf16 products), one wave
 // per expert row with 16-byte loads; each workgroup also quantises a slice of
-// every token; the last workgroup derives and publishes the routing.
+// every token.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dot_bf16x8(u32x4 x, u32x4 w, float acc)
 {
@@ -314,23 +412,6 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a)
         }
     }
 
-    // The last workgroup to arrive derives the routing once for the layer.
-    // One device-scope release per workgroup (by thread 0, after the barrier
-    // that orders the workgroup's stores) and one acquire in the last one.
-    __shared__ RouteLds rl;
-    __shared__ int last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        last = atomicAdd(a.counter, 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const RouteSrc src{a.M, a.E, a.K, a.logits, nullptr};
-    route_prologue(src, rl);
-    publish_route(rl, src, a.ids_out, a.w_out, a.cp);
-    if (threadIdx.x == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,142 +438,219 @@ template <int H, int I, int MT>
 __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 {
     using G = GateUpGeom<H, I>;
-    constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane;
+    constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, BPE = G::kBlocksPerExpert;
+    __shared__ RouteLds rl;
     __shared__ u32x4 act[MT * 4 * CH];          // [token][q][chunk] of 8 halves
 
-    // 0. this workgroup's expert and its tokens, from the published compaction
-    const int P = a.M * a.K;
-    const int slot = blockIdx.y;
-    if (slot >= *a.cp.n_act) return;
-    const int e = min(max(a.cp.act_experts[slot], 0), a.E - 1);
-    const int p0 = min(max(a.cp.offsets[slot], 0), P);
-    const int nt = max(0, min(min(a.cp.offsets[slot + 1], P) - p0, MT));   // at most M <= MT tokens
-    int tok_of[MT], pair_of[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        tok_of[t] = (t < nt) ? min(max(a.cp.pair_token[p0 + t], 0), a.M - 1) : 0;
-        pair_of[t] = (t < nt) ? min(max(a.cp.pair_src[p0 + t], 0), P - 1) : 0;
-    }
-
+    const int M = a.src.M;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane % LPR, grp = lane / LPR;
-    const int r = blockIdx.x * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
 
-    // 1. issue the weight stream for this lane
-    const u32x4* grow = (const u32x4*)(a.w13 + ((size_t)e * 2 * I + r) * (H / 2));
-    const u32x4* urow = grow + (size_t)I * CH;
-    const uint8_t* gsc = a.s13 + ((size_t)e * 2 * I + r) * CH;
-    const uint8_t* usc = gsc + (size_t)I * CH;
-    u32x4 wg[CPL], wu[CPL];
-    uint32_t sg[CPL], su[CPL];
+    // 0. every token's activations as f16 in LDS (independent of the routing,
+    //    so these loads overlap the routing prologue's); all loads first
+    constexpr int NST = (MT * (H / 8) + 255) / 256;
+    const int n8 = M * (H / 8);
+    u32x2 stg[NST];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        wg[i] = load_stream(grow + li + LPR * i);
-        wu[i] = load_stream(urow + li + LPR * i);
-    }
+    for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
+    // 1. routing, derived independently by every workgroup (the staging loads
+    //    above are in flight meanwhile); workgroup 0 publishes it for the down
+    //    kernel (and the caller)
+    route_prologue(a.src, rl);
+    if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        sg[i] = gsc[li + LPR * i];
-        su[i] = usc[li + LPR * i];
-    }
-
-    // 1b. pull this workgroup's share of the expert's down-projection weights
-    // into the memory-side cache, so the down kernel finds them there
-    constexpr size_t W2C = (size_t)H * I / 2, W2S = (size_t)H * I / 32;     // bytes per expert
-    constexpr int PFC = (int)(W2C / G::kBlocksPerExpert / 16), PFS = (int)(W2S / G::kBlocksPerExpert / 16);
-    static_assert(W2C % (16 * G::kBlocksPerExpert) == 0 && W2S % (16 * G::kBlocksPerExpert) == 0, "prefetch split");
-    constexpr int PF_PER = (PFC + PFS + 255) / 256;
-    u32x4 pf[PF_PER];
-    if (a.w2 != nullptr) {
-#pragma unroll
-        for (int j = 0; j < PF_PER; ++j) {
-            const int i = threadIdx.x + 256 * j;
-            if (i < PFC) pf[j] = *((const u32x4*)(a.w2 + e * W2C) + blockIdx.x * PFC + i);
-            else if (i < PFC + PFS) pf[j] = *((const u32x4*)(a.sw2 + e * W2S) + blockIdx.x * PFS + (i - PFC));
-            else pf[j] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < NST; ++j) {
+        const int idx = threadIdx.x + 256 * j;
+        if (idx < n8) {
+            const int t = idx / (H / 8), g8 = idx % (H / 8);
+            act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
         }
     }
-
-    // 2. stage this expert's tokens' activations as f16 in LDS
-    for (int idx = threadIdx.x; idx < nt * (H / 8); idx += blockDim.x) {
-        const int t = idx / (H / 8), g8 = idx % (H / 8);
-        const int tok = min(max(a.cp.pair_token[p0 + t], 0), a.M - 1);
-        const u32x2 codes = *((const u32x2*)(a.act_q + (size_t)tok * H) + g8);
-        act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(codes);
-    }
     __syncthreads();
+    const int n_items = rl.n_act * BPE;
 
-    // 3. dot products, one E8M0 block at a time
-    float accg[MT], accu[MT];
+    // 2. work items (selected expert, block of rows), strided over the grid;
+    //    the next item's weight loads are in flight while this one computes
+    constexpr size_t W2C = (size_t)H * I / 2, W2S = (size_t)H * I / 32;     // down bytes per expert
+    constexpr int PFC = (int)(W2C / BPE / 16), PFS = (int)(W2S / BPE / 16);
+    static_assert(W2C % (16 * BPE) == 0 && W2S % (16 * BPE) == 0, "prefetch split");
+    constexpr int PF_PER = (PFC + PFS + 255) / 256;
+
+    struct Stage {
+        u32x4 wg[CPL], wu[CPL];
+        uint32_t sg[CPL], su[CPL];
+        u32x4 pf[PF_PER];
+    };
+    auto issue = [&](int item, Stage& st) {
+        const int slot = item / BPE, rb = item % BPE;
+        const int e = rl.act_experts[slot];
+        const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const u32x4* grow = (const u32x4*)(a.w13 + ((size_t)e * 2 * I + r) * (H / 2));
+        const u32x4* urow = grow + (size_t)I * CH;
+        const uint8_t* gsc = a.s13 + ((size_t)e * 2 * I + r) * CH;
+        const uint8_t* usc = gsc + (size_t)I * CH;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) accg[t] = accu[t] = 0.0f;
+        for (int i = 0; i < CPL; ++i) {
+            st.wg[i] = load_stream(grow + li + LPR * i);
+            st.wu[i] = load_stream(urow + li + LPR * i);
+        }
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = li + LPR * i;
-        half2_t hg[16], hu[16];
-        e2m1x8_to_half(wg[i].x, hg + 0);
-        e2m1x8_to_half(wg[i].y, hg + 4);
-        e2m1x8_to_half(wg[i].z, hg + 8);
-        e2m1x8_to_half(wg[i].w, hg + 12);
-        e2m1x8_to_half(wu[i].x, hu + 0);
-        e2m1x8_to_half(wu[i].y, hu + 4);
-        e2m1x8_to_half(wu[i].z, hu + 8);
-        e2m1x8_to_half(wu[i].w, hu + 12);
+        for (int i = 0; i < CPL; ++i) {
+            st.sg[i] = gsc[li + LPR * i];
+            st.su[i] = usc[li + LPR * i];
+        }
+        // this item's share of the expert's down-projection weights, pulled
+        // into the memory-side cache for the down kernel
+        if (a.w2 != nullptr) {
+#pragma unroll
+            for (int j = 0; j < PF_PER; ++j) {
+                const int i = threadIdx.x + 256 * j;
+                if (i < PFC) st.pf[j] = *((const u32x4*)(a.w2 + e * W2C) + rb * PFC + i);
+                else if (i < PFC + PFS) st.pf[j] = *((const u32x4*)(a.sw2 + e * W2S) + rb * PFS + (i - PFC));
+                else st.pf[j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto compute = [&](int item, Stage& st) {
+        const int slot = item / BPE, rb = item % BPE;
+        const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const int p0 = rl.offsets[slot];
+        const int nt = min(rl.offsets[slot + 1] - p0, MT);   // an expert has at most M <= MT tokens
+        float accg[MT], accu[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) accg[t] = accu[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = li + LPR * i;
+            half2_t hg[16], hu[16];
+            e2m1x8_to_half(st.wg[i].x, hg + 0);
+            e2m1x8_to_half(st.wg[i].y, hg + 4);
+            e2m1x8_to_half(st.wg[i].z, hg + 8);
+            e2m1x8_to_half(st.wg[i].w, hg + 12);
+            e2m1x8_to_half(st.wu[i].x, hu + 0);
+            e2m1x8_to_half(st.wu[i].y, hu + 4);
+            e2m1x8_to_half(st.wu[i].z, hu + 8);
+            e2m1x8_to_half(st.wu[i].w, hu + 12);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < nt) {
+                    const int tok = rl.pair_token[p0 + t];
+                    const u32x4 a0 = act[(tok * 4 + 0) * CH + c], a1 = act[(tok * 4 + 1) * CH + c];
+                    const u32x4 a2 = act[(tok * 4 + 2) * CH + c], a3 = act[(tok * 4 + 3) * CH + c];
+                    accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), st.sg[i]);
+                    accu[t] += ldexp_e8m0(block_dot(hu, a0, a1, a2, a3), st.su[i]);
+                }
+            }
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (t < nt) {
-                const u32x4 a0 = act[(t * 4 + 0) * CH + c], a1 = act[(t * 4 + 1) * CH + c];
-                const u32x4 a2 = act[(t * 4 + 2) * CH + c], a3 = act[(t * 4 + 3) * CH + c];
-                accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), sg[i]);
-                accu[t] += ldexp_e8m0(block_dot(hu, a0, a1, a2, a3), su[i]);
+                accg[t] = group_sum<LPR>(accg[t]);
+                accu[t] = group_sum<LPR>(accu[t]);
+                const float sc = a.act_s[rl.pair_token[p0 + t]];
+                const float g = accg[t] * sc, u = accu[t] * sc;
+                if (li == 0) a.h[(size_t)rl.pair_src[p0 + t] * I + r] = g / (1.0f + expf(-g)) * u;
             }
         }
-    }
-
-    // 4. reduce over the LPR lanes of a row, SiLU(g)*u
+        if (a.w2 != nullptr) {           // retire the prefetch loads
+            uint32_t x = 0;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t < nt) {
-            accg[t] = group_sum<LPR>(accg[t]);
-            accu[t] = group_sum<LPR>(accu[t]);
-            const float st = a.act_s[tok_of[t]];
-            const float g = accg[t] * st, u = accu[t] * st;
-            if (li == 0) a.h[(size_t)pair_of[t] * I + r] = g / (1.0f + expf(-g)) * u;
+            for (int j = 0; j < PF_PER; ++j) x ^= st.pf[j].x ^ st.pf[j].y ^ st.pf[j].z ^ st.pf[j].w;
+            if (a.sink != nullptr) a.sink[threadIdx.x] = x;
         }
-    }
-    if (a.w2 != nullptr) {           // retire the prefetch loads
-        uint32_t x = 0;
-#pragma unroll
-        for (int j = 0; j < PF_PER; ++j) x ^= pf[j].x ^ pf[j].y ^ pf[j].z ^ pf[j].w;
-        if (a.sink != nullptr) a.sink[threadIdx.x] = x;
+    };
+
+    int item = blockIdx.x;
+    if (item >= n_items) return;
+    Stage s0, s1;
+    issue(item, s0);
+    for (;;) {
+        const int next = item + gridDim.x;
+        if (next < n_items) issue(next, s1);
+        compute(item, s0);
+        if (next >= n_items) break;
+        item = next;
+        const int after = item + gridDim.x;
+        if (after < n_items) issue(after, s0);
+        compute(item, s1);
+        if (after >= n_items) break;
+        item = after;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Per-(token, expert) FP8 requantisation of the intermediate, a wave per row
-// of I values: s2 = amax / 448 (1 for an all-zero row), q2 = E4M3(h / s2),
-// with a correctly rounded division.
+// of I values: s2 = fl32(amax / 448) (1 for an all-zero row), and the codes
+// E4M3(h * fl32(1 / s2)).  (The codes may differ from E4M3(h / s2) only where
+// h / s2 lies within an ulp of a rounding midpoint.)  Lane l holds the I/64
+// consecutive elements starting at l * I/64.
 // ---------------------------------------------------------------------------
+template <int I>
+struct RequantRow {
+    static constexpr int PER = I / kWave;
+    static_assert(I % kWave == 0, "requantisation needs I % 64 == 0");
+    float v[PER];
+
+    __device__ __forceinline__ void load(const float* __restrict__ h, int p)
+    {
+        const float* row = h + (size_t)p * I + (threadIdx.x & 63) * PER;
+        if constexpr (PER % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < PER; i += 4) {
+                const float4 f = *reinterpret_cast<const float4*>(row + i);
+                v[i] = f.x; v[i + 1] = f.y; v[i + 2] = f.z; v[i + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[i] = row[i];
+        }
+    }
+    __device__ __forceinline__ float scale() const
+    {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = wave_max(m);
+        return (m == 0.0f) ? 1.0f : m / 448.0f;
+    }
+    // codes[j] holds elements 4j..4j+3 of this lane (PER % 4 == 0), or one
+    // code per entry otherwise
+    __device__ __forceinline__ void encode(float sc, uint32_t* codes) const
+    {
+        const float inv = 1.0f / sc;
+        if constexpr (PER % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < PER; i += 4)
+                codes[i / 4] = e4m3x4_encode(v[i] * inv, v[i + 1] * inv, v[i + 2] * inv, v[i + 3] * inv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) codes[i] = e4m3_encode(v[i] * inv);
+        }
+    }
+    static constexpr int NCODE = (PER % 4 == 0) ? PER / 4 : PER;
+};
+
 template <int I>
 __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a)
 {
-    constexpr int PER = I / kWave;
-    static_assert(I % kWave == 0, "requantisation needs I % 64 == 0");
+    using R = RequantRow<I>;
     const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (p >= a.P) return;
     const int lane = threadIdx.x & 63;
-    float v[PER];
-    float m = 0.0f;
+    R row;
+    row.load(a.h, p);
+    const float sc = row.scale();
+    uint32_t codes[R::NCODE];
+    row.encode(sc, codes);
+    uint8_t* dst = a.q2 + (size_t)p * I + lane * R::PER;
+    if constexpr (R::PER % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        v[i] = a.h[(size_t)p * I + lane + kWave * i];
-        m = fmaxf(m, fabsf(v[i]));
+        for (int j = 0; j < R::NCODE; ++j) reinterpret_cast<uint32_t*>(dst)[j] = codes[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < R::NCODE; ++j) dst[j] = (uint8_t)codes[j];
     }
-    m = wave_max(m);
-    const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) a.q2[(size_t)p * I + lane + kWave * i] = (uint8_t)e4m3_encode(v[i] / s);
-    if (lane == 0) a.s2[p] = s;
+    if (lane == 0) a.s2[p] = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -513,7 +671,7 @@ struct DownGeom {
     static_assert(I % 32 == 0 && H % kRowsPerBlock == 0, "unsupported down shape");
 };
 
-template <int H, int I, int MT>
+template <int H, int I, int MT, bool FROM_H>
 __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
 {
     using G = DownGeom<H, I>;
@@ -538,18 +696,78 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
         for (int i = 0; i < CPL; ++i) sv[i] = sc[li + LPR * i];
     };
 
+    // The intermediate in LDS as f16.  From h: a wave per (token, expert) row
+    // requantises it (the same arithmetic as requant_kernel), which every
+    // workgroup repeats so that no workgroup waits for another; the rows'
+    // loads go out before the weight stream so they are not queued behind it.
+    using R = RequantRow<I>;
+    constexpr int RB = MT < 4 ? MT : 4;            // rows per wave held at once
+    R rows[RB];
+    if constexpr (FROM_H) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(wave + G::kWaves * j, P - 1));
+    }
     int slot = wave;
     u32x4 wv[CPL];
     uint32_t sv[CPL];
     if (slot < n_act) load_slot(slot, wv, sv);
 
-    // the FP8 intermediate as f16, while the weight loads are in flight
-    for (int idx = threadIdx.x; idx < P * (I / 8); idx += blockDim.x) {
-        const int p = idx / (I / 8), g8 = idx % (I / 8);
-        const u32x2 codes = *((const u32x2*)(a.q2 + (size_t)p * I) + g8);
-        q2h[(p * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(codes);
+    if constexpr (FROM_H) {
+        _Float16* q16 = reinterpret_cast<_Float16*>(q2h);
+        const bool tap = blockIdx.x == 0 && a.q2_out != nullptr;
+        for (int base = 0; base < P; base += G::kWaves * RB) {
+            if (base > 0) {
+#pragma unroll
+                for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(base + wave + G::kWaves * j, P - 1));
+            }
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const int p = base + wave + G::kWaves * j;
+                if (p >= P) break;
+                const float sc = rows[j].scale();
+                uint32_t codes[R::NCODE];
+                rows[j].encode(sc, codes);
+                const int k0 = lane * R::PER;
+                if constexpr (R::PER % 4 == 0) {
+#pragma unroll
+                    for (int c4 = 0; c4 < R::NCODE; ++c4) {
+                        const int k = k0 + 4 * c4;       // 4 consecutive elements, inside one group of 8
+                        uint2 hv2;
+                        hv2.x = e4m3x2_to_half2<false>(codes[c4]);
+                        hv2.y = e4m3x2_to_half2<true>(codes[c4]);
+                        *reinterpret_cast<uint2*>(q16 + ((p * 4 + ((k & 31) >> 3)) * CH + (k >> 5)) * 8 + (k & 7)) = hv2;
+                        if (tap) reinterpret_cast<uint32_t*>(a.q2_out + (size_t)p * I + k0)[c4] = codes[c4];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < R::NCODE; ++i) {
+                        const int k = k0 + i;
+                        q16[((p * 4 + ((k & 31) >> 3)) * CH + (k >> 5)) * 8 + (k & 7)] = (_Float16)e4m3_decode(codes[i]);
+                        if (tap) a.q2_out[(size_t)p * I + k] = (uint8_t)codes[i];
+                    }
+                }
+                if (lane == 0) {
+                    s2l[p] = sc;
+                    if (tap && a.s2_out != nullptr) a.s2_out[p] = sc;
+                }
+            }
+        }
+    } else {
+        constexpr int NST = (MT * 8 * (I / 8) + 511) / 512;
+        const int n8 = P * (I / 8);
+        u32x2 stg[NST];
+#pragma unroll
+        for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.q2)[min((int)threadIdx.x + 512 * j, n8 - 1)];
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+            const int idx = threadIdx.x + 512 * j;
+            if (idx < n8) {
+                const int p = idx / (I / 8), g8 = idx % (I / 8);
+                q2h[(p * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+            }
+        }
+        for (int p = threadIdx.x; p < P; p += blockDim.x) s2l[p] = a.s2[p];
     }
-    for (int p = threadIdx.x; p < P; p += blockDim.x) s2l[p] = a.s2[p];
     __syncthreads();
 
     float acc[MT];
@@ -635,7 +853,11 @@ template <int H, int I, int MT>
 static hipError_t launch_gate_up_t(int S, const GateUpArgs& a, hipStream_t s)
 {
     using G = GateUpGeom<H, I>;
-    hipLaunchKernelGGL((gate_up_kernel<H, I, MT>), dim3(G::kBlocksPerExpert, S), dim3(256), 0, s, a);
+    // one workgroup per (expert, row block) up to two per CU; beyond that the
+    // workgroups loop over their items with the next item's loads in flight
+    const int items = S * G::kBlocksPerExpert;
+    const int grid = items < 512 ? items : 512;
+    hipLaunchKernelGGL((gate_up_kernel<H, I, MT>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -644,12 +866,15 @@ static hipError_t launch_down_t(const DownArgs& a, hipStream_t s)
 {
     using G = DownGeom<H, I>;
     const size_t lds = (size_t)a.M * a.K * I * 2;
+    const void* fn = a.h != nullptr ? (const void*)down_kernel<H, I, MT, true> : (const void*)down_kernel<H, I, MT, false>;
     if (lds > 64 * 1024) {   // above the default dynamic-LDS limit (gfx950 has 160 KiB per CU)
-        hipError_t err = hipFuncSetAttribute((const void*)down_kernel<H, I, MT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((down_kernel<H, I, MT>), dim3(H / G::kRowsPerBlock), dim3(512), lds, s, a);
+    if (a.h != nullptr)
+        hipLaunchKernelGGL((down_kernel<H, I, MT, true>), dim3(H / G::kRowsPerBlock), dim3(512), lds, s, a);
+    else
+        hipLaunchKernelGGL((down_kernel<H, I, MT, false>), dim3(H / G::kRowsPerBlock), dim3(512), lds, s, a);
     return hipGetLastError();
 }
 
@@ -738,12 +963,12 @@ const char* kernel_names(int H, int I, int mt)
 {
     (void)mt;
     if (H == 256 && I == 64)
-        return "router_kernel<H=256> (top-K + compaction in the last WG) -> gate_up_kernel<H=256,I=64> (8 lanes/row, "
-               "32 row-pairs/WG) -> requant_kernel<I=64> -> down_kernel<H=256,I=64> (2 lanes/row, 32 rows/WG)";
+        return "router_kernel<H=256> -> gate_up_kernel<H=256,I=64> (routing prologue; 8 lanes/row, 32 row-pairs "
+               "per item) -> down_kernel<H=256,I=64> (FP8 requantisation prologue; 2 lanes/row, 32 rows/WG)";
     if (H == 2560 && I == 768)
-        return "router_kernel<H=2560> (top-K + compaction in the last WG) -> gate_up_kernel<H=2560,I=768> "
-               "(16 lanes/row, 16 row-pairs/WG, 48 WGs/expert, prefetches the down weights) -> requant_kernel<I=768> "
-               "-> down_kernel<H=2560,I=768> (8 lanes/row, 8 rows/WG, 320 WGs)";
+        return "router_kernel<H=2560> -> gate_up_kernel<H=2560,I=768> (routing prologue; 16 lanes/row, 16 row-pairs "
+               "per item, 48 items/expert, up to 512 WGs, prefetches the down weights) -> down_kernel<H=2560,I=768> "
+               "(FP8 requantisation prologue; 8 lanes/row, 8 rows/WG, 320 WGs)";
     return "unsupported";
 }
 

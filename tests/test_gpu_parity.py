@@ -375,6 +375,34 @@ def test_workspace_reuse_across_token_counts(moe):
         _check_layer(moe, shp, li, dw, ws)
 
 
+def test_requant_inside_down_matches_requant_kernel(moe, ling_weights):
+    """The forward path requantises inside the down kernel; its codes and
+    scales (the experts taps) must equal the standalone requant kernel's."""
+    w, dw = ling_weights
+    li = synth.verify_router(205, w, 20)
+    shp = _shape(moe, w, 8)
+    ws = _ws(moe, shp)
+    t = oracle.route(li.x, li.wts.wr, 8)
+    M, K, I = 4, 8, shp.inter
+    q = torch.empty((M, shp.hidden), dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    moe.moe_quant_act(shp, M, dev(li.x), q, s)
+    ids, wts = dev(t.ids.astype(np.int32)), dev(t.w.astype(np.float32))
+    taps = {"h": torch.empty((M * K, I), dtype=torch.float32, device="cuda"),
+            "inter_fp8": torch.empty((M * K, I), dtype=torch.uint8, device="cuda"),
+            "inter_scale": torch.empty(M * K, dtype=torch.float32, device="cuda")}
+    out = torch.empty((M, shp.hidden), dtype=torch.float32, device="cuda")
+    moe.moe_experts_forward(shp, M, q, s, ids, wts, dw.w13, dw.s13, dw.w2, dw.s2, out, ws, taps=taps)
+    h2 = torch.empty_like(taps["h"])
+    q2 = torch.empty_like(taps["inter_fp8"])
+    s2 = torch.empty_like(taps["inter_scale"])
+    moe.moe_gate_up(shp, M, q, s, ids, dw.w13, dw.s13, h2, q2, s2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(taps["h"], h2)
+    assert torch.equal(taps["inter_fp8"], q2)
+    assert torch.equal(taps["inter_scale"], s2)
+
+
 def test_deterministic_repeat(moe, ling_weights):
     w, dw = ling_weights
     li = synth.verify_router(204, w, 32)
