@@ -16,8 +16,10 @@ Reported (one JSON line on stdout):
                router, x and out) / wall time
   us_per_layer wall time per layer
   m4           the same at 4 tokens (the speculative-decoding verify window)
-  roofline     the gate/up kernel (the largest byte stream) against 8 TB/s,
-               from HIP events recorded around it inside the replayed graphs
+  roofline     the gate/up kernel (the largest byte stream) against 8 TB/s:
+               its algorithmic bytes (the selected experts' gate/up codes and
+               scales) over its execution time, from start/stop HIP events its
+               launch stamps (plain launches on the bench stream)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -58,6 +60,9 @@ def parse():
     p.add_argument("--reps", type=int, default=8, help="independent hidden sets (one graph each)")
     p.add_argument("--plain-steps", type=int, default=2000, help="layer forwards timed with plain launches")
     p.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU baseline (0: skip)")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
+    p.add_argument("--tokens", type=str, default="1,4", help="token counts to time (the first is the reported value)")
     return p.parse_args()
 
 
@@ -75,6 +80,14 @@ def main() -> int:
     from mxfp4_weight_streaming_amd import synth
 
     torch.cuda.set_device(0)
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: {args.copy_mb} MiB x 3")
+        del src, dst
     shp = moe.shape(H, I, E, K)
     L, reps = args.layers, args.reps
     st, path = moe.moe_path_info(shp, 1)
@@ -96,18 +109,23 @@ def main() -> int:
 
     results = {}
     kernel_stats = {}
-    for M in (1, 4):
+    token_counts = [int(v) for v in args.tokens.split(",")]
+    for M in token_counts:
         xs = synth.device_hidden(L * reps, M, H, seed=10_000 + M)
         # routing pre-pass: distinct experts of every (hidden set, layer)
         ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
         wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
-        n_active = torch.empty(1, dtype=torch.int32, device="cuda")
-        n_act = np.zeros((reps, L), np.int64)
+        n_active = torch.zeros((reps, L), dtype=torch.int32, device="cuda")
         with torch.cuda.stream(stream):
             for r in range(reps):
                 for l in range(L):
-                    moe.moe_route(shp, M, xs[r * L + l], stack[l]["wr"], ids, wts, ws, taps={"n_active": n_active})
-                    n_act[r, l] = int(n_active.item())
+                    moe.moe_route(shp, M, xs[r * L + l], stack[l]["wr"], ids, wts, ws,
+                                  taps={"n_active": n_active[r, l:l + 1]})
+        torch.cuda.synchronize()
+        n_act = n_active.cpu().numpy().astype(np.int64)
+        if n_act.min() < K or n_act.max() > min(E, M * K):
+            raise RuntimeError(f"routing pre-pass read back distinct-expert counts outside [{K}, {min(E, M * K)}]: "
+                               f"min {n_act.min()}, max {n_act.max()}")
         rep_bytes = [sum(layer_bytes(int(n_act[r, l]), M) for l in range(L)) for r in range(reps)]
 
         with torch.cuda.stream(stream):
@@ -160,28 +178,29 @@ def main() -> int:
             torch.cuda.synchronize()
         pms = p0.elapsed_time(p1)
 
-        # per-kernel durations from HIP events recorded between the kernels of
-        # each layer, in plain launches; a spin kernel at the head of the
-        # stream lets the host queue the whole walk first, so the kernels run
-        # back to back and the events see no host gaps
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+        # per-kernel durations from start/stop HIP events that each kernel's
+        # launch stamps with its own execution interval (plain launches; a
+        # spin kernel at the head of the stream lets the host queue the whole
+        # walk first, so the kernels run back to back as in the timed walk)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
         dur = {"router": [], "gate_up": [], "down": []}
         with torch.cuda.stream(stream):
             for row in evs:
                 for e in row:
                     e.record(stream)          # torch creates the HIP event on first record
+            gu_launch_bytes = []
             for ps in range(max(2, 400 // L)):
-                torch.cuda._sleep(50_000_000)
                 r = ps % reps
+                torch.cuda._sleep(50_000_000)
                 for l in range(L):
                     fwd(l, xs[r * L + l], M, events=evs[l])
                 torch.cuda.synchronize()
                 for l in range(L):
-                    dur["router"].append(evs[l][0].elapsed_time(evs[l][1]))
-                    dur["gate_up"].append(evs[l][1].elapsed_time(evs[l][2]))
-                    dur["down"].append(evs[l][2].elapsed_time(evs[l][3]))
+                    for k, name in enumerate(("router", "gate_up", "down")):
+                        dur[name].append(evs[l][2 * k].elapsed_time(evs[l][2 * k + 1]))
+                    gu_launch_bytes.append(int(n_act[r, l]) * W13_BYTES)
         kmean = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}   # microseconds
-        gu_bytes = float(np.mean(n_act[0])) * W13_BYTES
+        gu_bytes = float(np.mean(gu_launch_bytes))
         kernel_stats[M] = {"us": kmean, "gate_up_bytes": gu_bytes,
                            "gate_up_gbs": gu_bytes / (kmean["gate_up"] * 1e-6) / 1e9}
         log(f"M={M}: kernel means (us) {kmean}, gate_up {kernel_stats[M]['gate_up_gbs']:.0f} GB/s")
@@ -195,8 +214,18 @@ def main() -> int:
     if args.cpu_layers > 0:
         cpu = cpu_baseline(args.cpu_layers)
 
-    r1, r4 = results[1], results[4]
-    k1 = kernel_stats[1]
+    r1 = results[token_counts[0]]
+    k1 = kernel_stats[token_counts[0]]
+    m4 = None
+    if 4 in results:
+        r4 = results[4]
+        m4 = {"us_per_layer": round(r4["us_per_layer"], 3), "gbs": round(r4["gbs"], 1),
+              "pct_of_hbm_peak": round(100 * r4["gbs"] / HBM_PEAK_GBS, 2),
+              "mean_distinct_experts": round(r4["mean_distinct_experts"], 2),
+              "plain_us_per_layer": round(r4["plain_us_per_layer"], 3),
+              "kernel_us": {k: round(v, 3) for k, v in kernel_stats[4]["us"].items()},
+              "gate_up_gbs": round(kernel_stats[4]["gate_up_gbs"], 1)}
+    traffic = measured_traffic()
     line = {
         "metric": "MoE-layer decode us + weight-stream HBM GB/s (% of peak), M=1 and M=4",
         "value": round(r1["gbs"], 1),
@@ -216,21 +245,50 @@ def main() -> int:
         "us_per_layer": round(r1["us_per_layer"], 3),
         "pct_of_hbm_peak": round(100 * r1["gbs"] / HBM_PEAK_GBS, 2),
         "plain_launch": {"us_per_layer": round(r1["plain_us_per_layer"], 3), "gbs": round(r1["plain_gbs"], 1)},
-        "m4": {"us_per_layer": round(r4["us_per_layer"], 3), "gbs": round(r4["gbs"], 1),
-               "pct_of_hbm_peak": round(100 * r4["gbs"] / HBM_PEAK_GBS, 2),
-               "mean_distinct_experts": round(r4["mean_distinct_experts"], 2),
-               "plain_us_per_layer": round(r4["plain_us_per_layer"], 3),
-               "kernel_us": {k: round(v, 3) for k, v in kernel_stats[4]["us"].items()},
-               "gate_up_gbs": round(kernel_stats[4]["gate_up_gbs"], 1)},
+        "m4": m4,
         "kernel_us": {k: round(v, 3) for k, v in k1["us"].items()},
         "roofline": {"kernel": "gate_up_kernel<H=2560,I=768> (1 token)", "bound": "hbm",
                      "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+# HBM traffic of the gate/up kernel comes from hardware counters taken with
+# rocprofv3 (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
+# and is only reported while the kernel source is the one it was taken on.
+KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
+                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp"]
+TRAFFIC_FILE = "profiles/gate_up_hbm_traffic.txt"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(n_layers: int) -> dict:

@@ -134,11 +134,13 @@ moe_status moe_decode_forward(const moe_shape* shape, int32_t M,
                               const uint8_t* w2, const uint8_t* w2_scale,
                               float* out, void* ws, size_t ws_bytes, void* stream);
 
-/* moe_decode_forward that also records caller-created HIP events on `stream`
- * for per-kernel timing: events[0] before the router kernel, events[1] after
- * it, events[2] after the gate/up kernel, events[3] after the down kernel.
- * `events` (an array of 4 hipEvent_t) or any element may be NULL.  Usable
- * under stream capture (the records become graph event nodes). */
+/* moe_decode_forward with per-kernel timing: `events` is an array of 6
+ * caller-created hipEvent_t (timing enabled), start/stop pairs for the router
+ * (0, 1), gate/up (2, 3) and down (4, 5) kernels.  Each pair is stamped by the
+ * kernel's own launch (hipExtLaunchKernel), so hipEventElapsedTime of a pair
+ * is that kernel's execution time on the GPU, without queueing or dispatch
+ * gaps.  `events` may be NULL (then this is moe_decode_forward); a NULL pair
+ * launches that kernel without stamps.  Not for use under stream capture. */
 moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M,
                                      const uint16_t* hidden, const uint16_t* router_w,
                                      const uint8_t* w13, const uint8_t* w13_scale,

@@ -150,8 +150,11 @@ def moe_decode_forward(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, o
 
 def moe_decode_forward_events(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, events,
                               stream=None):
-    """events: 4 torch.cuda.Event (or None entries); recorded around the 3 kernels."""
-    arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+    """events: 6 torch.cuda.Event (timing enabled, each recorded once so that it
+    exists), start/stop pairs stamped by the router, gate/up and down launches."""
+    if len(events) != 6:
+        raise ValueError("moe_decode_forward_events takes 6 events (start/stop of 3 kernels)")
+    arr = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
     _check(_lib.moe_decode_forward_events(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
                                           _p(w2), _p(w2_scale), _p(out), _p(ws), _nbytes(ws), _stream(stream),
                                           arr),

@@ -103,10 +103,10 @@ int num_slots(const moe_shape* s, int32_t M)
 }
 
 moe_status enqueue_router(const moe_shape* s, int32_t M, const uint16_t* x, const uint16_t* wr, uint8_t* act_q,
-                          float* act_s, const Carved& c, hipStream_t st)
+                          float* act_s, const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {})
 {
     moe::RouterArgs a{x, wr, M, s->num_experts, c.at<float>(c.L.logits), act_q, act_s};
-    hipError_t e = moe::launch_router(s->hidden, token_bound(M), a, st);
+    hipError_t e = moe::launch_router(s->hidden, token_bound(M), a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "router launch");
 }
 
@@ -125,11 +125,12 @@ moe_status enqueue_topk(const moe_shape* s, int32_t M, bool from_logits, const i
 // from caller-given ids.
 moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const int32_t* ids, int32_t* ids_out, float* w_out,
                            const uint8_t* act_q, const float* act_s, const uint8_t* w13, const uint8_t* s13, float* h,
-                           const uint8_t* w2_prefetch, const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st)
+                           const uint8_t* w2_prefetch, const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st,
+                           const moe::LaunchEvents& ev = {})
 {
     const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids};
     moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, w2_prefetch, sw2_prefetch, nullptr};
-    hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st);
+    hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
 }
 
@@ -144,10 +145,10 @@ moe_status enqueue_requant(const moe_shape* s, int32_t M, const float* h, uint8_
 // caller's E4M3 intermediate q2/s2.
 moe_status enqueue_down(const moe_shape* s, int32_t M, const float* h, const uint8_t* q2, const float* s2,
                         uint8_t* q2_out, float* s2_out, const float* topk_w, const uint8_t* w2, const uint8_t* sw2,
-                        float* out, const Carved& c, hipStream_t st)
+                        float* out, const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {})
 {
     moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, h, q2, s2, q2_out, s2_out, topk_w, c.cp(), out};
-    hipError_t e = moe::launch_down(s->hidden, s->inter, token_bound(M), a, st);
+    hipError_t e = moe::launch_down(s->hidden, s->inter, token_bound(M), a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
 }
 
@@ -190,10 +191,9 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
     CHECK_ALIGN(hidden); CHECK_ALIGN(router_w); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    auto mark = [&](int i) -> moe_status {
-        if (events == nullptr || events[i] == nullptr) return MOE_OK;
-        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+    auto ev = [&](int k) -> moe::LaunchEvents {
+        if (events == nullptr) return {};
+        return {static_cast<hipEvent_t>(events[2 * k]), static_cast<hipEvent_t>(events[2 * k + 1])};
     };
     const Carved c = carve(shape, M, ws);
     int32_t* ids = c.at<int32_t>(c.L.ids);
@@ -201,15 +201,11 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
     uint8_t* q = c.at<uint8_t>(c.L.act_q);
     float* sc = c.at<float>(c.L.act_s);
     float* h = c.at<float>(c.L.h);
-    if ((st = mark(0)) != MOE_OK) return st;
-    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s)) != MOE_OK) return st;
-    if ((st = mark(1)) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, w2, w2_scale, c, s)) != MOE_OK)
+    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, w2, w2_scale, c, s, ev(1))) !=
+        MOE_OK)
         return st;
-    if ((st = mark(2)) != MOE_OK) return st;
-    if ((st = enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s)) != MOE_OK)
-        return st;
-    return mark(3);
+    return enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s, ev(2));
 }
 
 moe_status moe_decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,

@@ -116,14 +116,23 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     return L;
 }
 
+// Optional start/stop events of one kernel launch.  When either is set the
+// kernel goes through hipExtLaunchKernel, which stamps the events with the
+// kernel's own start and end on the GPU (no queueing or dispatch gaps).
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Launchers (moe_kernels.hip).  Each returns the hipError_t of its launch.
 // mt is the token bound the kernels are instantiated for (1, 2, 4 or 8).
 bool gemv_shape_supported(int H, int I);
-hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s);
+hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_quant(int H, const uint16_t* x, int M, uint8_t* q, float* sc, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s);  // S: slot bound
-hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s);
+hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s,
+                          const LaunchEvents& ev = {});  // S: slot bound
+hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);

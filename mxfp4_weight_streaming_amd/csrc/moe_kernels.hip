@@ -26,6 +26,8 @@
 // f16 operands, fp32 accumulation), not the matrix cores.
 //   [EN] = "NVIDIA Shows 3 Ways to Speed Up MoE Inference on DGX Spark,
 //          Lifting Ling-3.0-flash Throughput 42.5%"
+#include <hip/hip_ext.h>
+
 #include "device_common.hpp"
 #include "moe_internal.hpp"
 
@@ -849,20 +851,29 @@ bool gemv_shape_supported(int H, int I)
     return (H == 256 && I == 64) || (H == 2560 && I == 768);
 }
 
+template <typename F, typename... Args>
+static void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, const LaunchEvents& ev, Args... args)
+{
+    if (ev.start != nullptr || ev.stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
 template <int H, int I, int MT>
-static hipError_t launch_gate_up_t(int S, const GateUpArgs& a, hipStream_t s)
+static hipError_t launch_gate_up_t(int S, const GateUpArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
     using G = GateUpGeom<H, I>;
     // one workgroup per (expert, row block) up to two per CU; beyond that the
     // workgroups loop over their items with the next item's loads in flight
     const int items = S * G::kBlocksPerExpert;
     const int grid = items < 512 ? items : 512;
-    hipLaunchKernelGGL((gate_up_kernel<H, I, MT>), dim3(grid), dim3(256), 0, s, a);
+    launch(gate_up_kernel<H, I, MT>, dim3(grid), dim3(256), 0, s, ev, a);
     return hipGetLastError();
 }
 
 template <int H, int I, int MT>
-static hipError_t launch_down_t(const DownArgs& a, hipStream_t s)
+static hipError_t launch_down_t(const DownArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
     using G = DownGeom<H, I>;
     const size_t lds = (size_t)a.M * a.K * I * 2;
@@ -872,19 +883,19 @@ static hipError_t launch_down_t(const DownArgs& a, hipStream_t s)
         if (err != hipSuccess) return err;
     }
     if (a.h != nullptr)
-        hipLaunchKernelGGL((down_kernel<H, I, MT, true>), dim3(H / G::kRowsPerBlock), dim3(512), lds, s, a);
+        launch(down_kernel<H, I, MT, true>, dim3(H / G::kRowsPerBlock), dim3(512), (uint32_t)lds, s, ev, a);
     else
-        hipLaunchKernelGGL((down_kernel<H, I, MT, false>), dim3(H / G::kRowsPerBlock), dim3(512), lds, s, a);
+        launch(down_kernel<H, I, MT, false>, dim3(H / G::kRowsPerBlock), dim3(512), (uint32_t)lds, s, ev, a);
     return hipGetLastError();
 }
 
 template <int H, int MT>
-static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s)
+static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
     // one wave per expert row; workgroup t also quantises token t, so there
     // are at least M workgroups
     const int blocks = (a.E + 3) / 4 > a.M ? (a.E + 3) / 4 : a.M;
-    hipLaunchKernelGGL((router_kernel<H, MT>), dim3(blocks), dim3(256), 0, s, a);
+    launch(router_kernel<H, MT>, dim3(blocks), dim3(256), 0, s, ev, a);
     return hipGetLastError();
 }
 
@@ -897,10 +908,10 @@ static hipError_t launch_router_t(const RouterArgs& a, hipStream_t s)
         default: return hipErrorInvalidValue;              \
     }
 
-hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s)
+hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    if (H == 256) { MOE_DISPATCH_MT(mt, (launch_router_t<256, MTc>(a, s))) }
-    if (H == 2560) { MOE_DISPATCH_MT(mt, (launch_router_t<2560, MTc>(a, s))) }
+    if (H == 256) { MOE_DISPATCH_MT(mt, (launch_router_t<256, MTc>(a, s, ev))) }
+    if (H == 2560) { MOE_DISPATCH_MT(mt, (launch_router_t<2560, MTc>(a, s, ev))) }
     return hipErrorInvalidValue;
 }
 
@@ -918,17 +929,17 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s)
+hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    if (H == 256 && I == 64) { MOE_DISPATCH_MT(mt, (launch_gate_up_t<256, 64, MTc>(S, a, s))) }
-    if (H == 2560 && I == 768) { MOE_DISPATCH_MT(mt, (launch_gate_up_t<2560, 768, MTc>(S, a, s))) }
+    if (H == 256 && I == 64) { MOE_DISPATCH_MT(mt, (launch_gate_up_t<256, 64, MTc>(S, a, s, ev))) }
+    if (H == 2560 && I == 768) { MOE_DISPATCH_MT(mt, (launch_gate_up_t<2560, 768, MTc>(S, a, s, ev))) }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s)
+hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    if (H == 256 && I == 64) { MOE_DISPATCH_MT(mt, (launch_down_t<256, 64, MTc>(a, s))) }
-    if (H == 2560 && I == 768) { MOE_DISPATCH_MT(mt, (launch_down_t<2560, 768, MTc>(a, s))) }
+    if (H == 256 && I == 64) { MOE_DISPATCH_MT(mt, (launch_down_t<256, 64, MTc>(a, s, ev))) }
+    if (H == 2560 && I == 768) { MOE_DISPATCH_MT(mt, (launch_down_t<2560, 768, MTc>(a, s, ev))) }
     return hipErrorInvalidValue;
 }
 
