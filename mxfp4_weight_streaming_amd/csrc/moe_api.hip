@@ -56,10 +56,16 @@ moe_status check_shape(const moe_shape* s, int32_t M)
     if (!moe::gemv_shape_supported(s->hidden, s->inter))
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "(H=%d, I=%d) is not a compiled shape; compiled: (256,64), (2560,768)",
                     s->hidden, s->inter);
-    if (M > moe::kMaxGemvTokens)
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "M=%d above %d tokens is not compiled", M, moe::kMaxGemvTokens);
+    if (M > moe::kMaxChunkTokens)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "M=%d above %d tokens is not compiled", M, moe::kMaxChunkTokens);
+    if (M > moe::kMaxGemvTokens && !moe::chunk_shape_supported(s->hidden, s->inter, s->num_experts))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "the chunk path (M > %d) needs E %% 16 == 0 (E=%d)",
+                    moe::kMaxGemvTokens, s->num_experts);
     return MOE_OK;
 }
+
+// M above the GEMV bound takes the chunk path (grouped MFMA contractions).
+bool chunked(int32_t M) { return M > moe::kMaxGemvTokens; }
 
 moe_status check_ws(const moe_shape* s, int32_t M, void* ws, size_t ws_bytes)
 {
@@ -152,6 +158,85 @@ moe_status enqueue_down(const moe_shape* s, int32_t M, const float* h, const uin
     return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
 }
 
+// ---- chunk path ----------------------------------------------------------
+moe_status enqueue_chunk_router(const moe_shape* s, int32_t M, const uint16_t* x, const uint16_t* wr, const Carved& c,
+                                hipStream_t st, const moe::LaunchEvents& ev = {})
+{
+    moe::ChunkRouterArgs a{x, wr, M, s->num_experts, c.at<float>(c.L.logits)};
+    hipError_t e = moe::launch_chunk_router(s->hidden, a, st, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk router launch");
+}
+
+moe_status enqueue_quant(const moe_shape* s, int32_t M, const uint16_t* x, uint8_t* q, float* sc, hipStream_t st)
+{
+    hipError_t e = moe::launch_quant(s->hidden, x, M, q, sc, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "quant launch");
+}
+
+moe_status enqueue_chunk_topk(const moe_shape* s, int32_t M, int32_t* ids, float* w, const Carved& c, hipStream_t st)
+{
+    moe::ChunkTopkArgs a{c.at<float>(c.L.logits), M, s->num_experts, s->topk, ids, w};
+    hipError_t e = moe::launch_chunk_topk(a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk topk launch");
+}
+
+moe_status enqueue_sort(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st)
+{
+    moe::SortArgs a{ids, M, s->topk, s->num_experts, c.cp(), c.at<int32_t>(c.L.pos_of)};
+    hipError_t e = moe::launch_sort_pairs(a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "pair sort launch");
+}
+
+moe_status enqueue_chunk_gate_up(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
+                                 const uint8_t* w13, const uint8_t* s13, const Carved& c, hipStream_t st,
+                                 const moe::LaunchEvents& ev = {})
+{
+    moe::ChunkGateUpArgs a{c.cp(), w13, s13, act_q, act_s, c.at<float>(c.L.h)};
+    hipError_t e = moe::launch_chunk_gate_up(s->hidden, s->inter, num_slots(s, M), a, st, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk gate_up launch");
+}
+
+moe_status enqueue_chunk_down(const moe_shape* s, int32_t M, const uint8_t* q2, const float* s2, bool by_pair,
+                              const float* topk_w, const uint8_t* w2, const uint8_t* sw2, const Carved& c,
+                              hipStream_t st, const moe::LaunchEvents& ev = {})
+{
+    moe::ChunkDownArgs a{c.cp(), w2, sw2, q2, s2, by_pair ? 1 : 0, topk_w, c.at<float>(c.L.y)};
+    hipError_t e = moe::launch_chunk_down(s->hidden, s->inter, num_slots(s, M), a, st, ev);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk down launch");
+}
+
+moe_status enqueue_combine(const moe_shape* s, int32_t M, float* out, const Carved& c, hipStream_t st)
+{
+    moe::CombineArgs a{c.at<float>(c.L.y), c.at<int32_t>(c.L.pos_of), M, s->topk, out};
+    hipError_t e = moe::launch_combine(s->hidden, a, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+}
+
+// Rows of a sorted-order intermediate, delivered in pair order.
+moe_status gather_out(void* dst, const void* src, int32_t M, int K, int row_bytes, const Carved& c, hipStream_t st)
+{
+    if (dst == nullptr) return MOE_OK;
+    hipError_t e = moe::launch_gather_rows(src, dst, c.at<int32_t>(c.L.pos_of), M * K, row_bytes, st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "tap gather");
+}
+
+// Gate/up -> requantisation -> down -> combine over sorted pairs (the sort
+// has run).  h, q2 and s2 stay in the workspace in sorted order.
+moe_status enqueue_chunk_experts(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
+                                 const float* topk_w, const uint8_t* w13, const uint8_t* s13, const uint8_t* w2,
+                                 const uint8_t* sw2, float* out, const Carved& c, hipStream_t st,
+                                 const moe::LaunchEvents& ev_gate_up = {}, const moe::LaunchEvents& ev_down = {})
+{
+    moe_status r;
+    if ((r = enqueue_chunk_gate_up(s, M, act_q, act_s, w13, s13, c, st, ev_gate_up)) != MOE_OK) return r;
+    if ((r = enqueue_requant(s, M, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), st)) != MOE_OK)
+        return r;
+    if ((r = enqueue_chunk_down(s, M, c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), false, topk_w, w2, sw2, c, st,
+                                ev_down)) != MOE_OK)
+        return r;
+    return enqueue_combine(s, M, out, c, st);
+}
+
 moe_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st)
 {
     if (dst == nullptr || bytes == 0) return MOE_OK;
@@ -201,6 +286,13 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
     uint8_t* q = c.at<uint8_t>(c.L.act_q);
     float* sc = c.at<float>(c.L.act_s);
     float* h = c.at<float>(c.L.h);
+    if (chunked(M)) {
+        if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s, ev(0))) != MOE_OK) return st;
+        if ((st = enqueue_quant(shape, M, hidden, q, sc, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_topk(shape, M, ids, w, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_sort(shape, M, ids, c, s)) != MOE_OK) return st;
+        return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2));
+    }
     if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
     if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, w2, w2_scale, c, s, ev(1))) !=
         MOE_OK)
@@ -231,8 +323,15 @@ moe_status moe_route(const moe_shape* shape, int32_t M, const uint16_t* hidden, 
     float* act_s = taps ? taps->act_scale : nullptr;
     if ((act_q == nullptr) != (act_s == nullptr))
         return fail(MOE_ERR_INVALID_ARG, "taps act_fp8 and act_scale must be given together");
-    if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, c, s)) != MOE_OK) return st;
-    if ((st = enqueue_topk(shape, M, true, nullptr, topk_ids, topk_w, c, s)) != MOE_OK) return st;
+    if (chunked(M)) {
+        if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s)) != MOE_OK) return st;
+        if (act_q != nullptr && (st = enqueue_quant(shape, M, hidden, act_q, act_s, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_topk(shape, M, topk_ids, topk_w, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+    } else {
+        if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_topk(shape, M, true, nullptr, topk_ids, topk_w, c, s)) != MOE_OK) return st;
+    }
     if (taps == nullptr) return MOE_OK;
     const size_t P = (size_t)M * shape->topk, S = (size_t)num_slots(shape, M);
     if ((st = copy_out(taps->logits, c.at<void>(c.L.logits), (size_t)M * shape->num_experts * 4, s)) != MOE_OK) return st;
@@ -266,6 +365,17 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M, const uint8_t*
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
+    if (chunked(M)) {
+        if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_experts(shape, M, act_fp8, act_scale, topk_w, w13, w13_scale, w2, w2_scale, out, c,
+                                        s)) != MOE_OK)
+            return st;
+        if (taps == nullptr) return MOE_OK;
+        const int I = shape->inter, K = shape->topk;
+        if ((st = gather_out(taps->h, c.at<void>(c.L.h), M, K, I * 4, c, s)) != MOE_OK) return st;
+        if ((st = gather_out(taps->inter_fp8, c.at<void>(c.L.q2), M, K, I, c, s)) != MOE_OK) return st;
+        return gather_out(taps->inter_scale, c.at<void>(c.L.s2), M, K, 4, c, s);
+    }
     float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
     uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
     float* s2_tap = taps ? taps->inter_scale : nullptr;
@@ -287,6 +397,17 @@ moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
+    if (chunked(M)) {
+        if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_requant(shape, M, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), s)) !=
+            MOE_OK)
+            return st;
+        const int I = shape->inter, K = shape->topk;
+        if ((st = gather_out(h, c.at<void>(c.L.h), M, K, I * 4, c, s)) != MOE_OK) return st;
+        if ((st = gather_out(inter_fp8, c.at<void>(c.L.q2), M, K, I, c, s)) != MOE_OK) return st;
+        return gather_out(inter_scale, c.at<void>(c.L.s2), M, K, 4, c, s);
+    }
     if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, nullptr,
                               nullptr, c, s)) != MOE_OK)
         return st;
@@ -305,6 +426,12 @@ moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* in
     if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Carved c = carve(shape, M, ws);
+    if (chunked(M)) {
+        if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_down(shape, M, inter_fp8, inter_scale, true, topk_w, w2, w2_scale, c, s)) != MOE_OK)
+            return st;
+        return enqueue_combine(shape, M, out, c, s);
+    }
     if ((st = enqueue_topk(shape, M, false, topk_ids, nullptr, nullptr, c, s)) != MOE_OK) return st;
     return enqueue_down(shape, M, nullptr, inter_fp8, inter_scale, nullptr, nullptr, topk_w, w2, w2_scale, out, c, s);
 }
@@ -323,6 +450,9 @@ moe_status moe_path_info(const moe_shape* shape, int32_t M, char* buf, size_t le
     if (buf != nullptr && len > 0) {
         if (st != MOE_OK)
             snprintf(buf, len, "unsupported: %s", g_last_error);
+        else if (chunked(M))
+            snprintf(buf, len, "chunk path, M=%d, E=%d, K=%d: %s", M, shape->num_experts, shape->topk,
+                     moe::chunk_kernel_names(shape->hidden, shape->inter));
         else
             snprintf(buf, len, "gemv path, M=%d (token bound %d), E=%d, K=%d: %s", M, token_bound(M),
                      shape->num_experts, shape->topk, moe::kernel_names(shape->hidden, shape->inter, token_bound(M)));

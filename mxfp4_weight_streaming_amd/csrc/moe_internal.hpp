@@ -14,6 +14,10 @@ constexpr int kMaxGemvTokens = 8;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxPairs = kMaxGemvTokens * kMaxTopK;
+// Largest token count of the chunk path (M > kMaxGemvTokens): its M*K pairs
+// are sorted by expert in one workgroup's LDS.
+constexpr int kMaxChunkTokens = 2048;
+constexpr int kMaxChunkPairs = kMaxChunkTokens * kMaxTopK;
 
 // Token -> expert compaction as published in the workspace.
 struct Compaction {
@@ -84,10 +88,62 @@ struct RequantArgs {
     float* s2;             // [P]
 };
 
+// Chunk path (M > kMaxGemvTokens): grouped contractions over the expert-sorted
+// pairs.  "Sorted position" pos indexes the pairs in (expert, pair index)
+// order, as in Compaction; pos_of[p] is the sorted position of pair p.
+struct ChunkRouterArgs {
+    const uint16_t* x;     // [M,H] bf16
+    const uint16_t* wr;    // [E,H] bf16
+    int M, E;
+    float* logits;         // [M,E]
+};
+
+struct ChunkTopkArgs {
+    const float* logits;   // [M,E]
+    int M, E, K;
+    int32_t* ids;          // [M,K]
+    float* w;              // [M,K]
+};
+
+struct SortArgs {
+    const int32_t* ids;    // [M,K]; out-of-range ids are clamped into [0, E)
+    int M, K, E;
+    Compaction cp;         // written
+    int32_t* pos_of;       // [M*K]
+};
+
+struct ChunkGateUpArgs {
+    Compaction cp;         // read
+    const uint8_t* w13;    // [E,2I,H/2]
+    const uint8_t* s13;    // [E,2I,H/32]
+    const uint8_t* act_q;  // [M,H]
+    const float* act_s;    // [M]
+    float* h;              // [M*K,I] in sorted order
+};
+
+struct ChunkDownArgs {
+    Compaction cp;         // read
+    const uint8_t* w2;     // [E,H,I/2]
+    const uint8_t* sw2;    // [E,H,I/32]
+    const uint8_t* q2;     // [M*K,I] E4M3 intermediate
+    const float* s2;       // [M*K]
+    int by_pair;           // 0: q2/s2 rows in sorted order; 1: in pair order
+    const float* topk_w;   // [M*K] router weights in pair order
+    float* y;              // [M*K,H] weighted expert outputs in sorted order
+};
+
+struct CombineArgs {
+    const float* y;        // [M*K,H] sorted order
+    const int32_t* pos_of; // [M*K]
+    int M, K;
+    float* out;            // [M,H]
+};
+
 // Workspace carving.  No state is carried between calls: every call writes
-// what it later reads.
+// what it later reads.  pos_of and y exist only for the chunk path.
 struct WsLayout {
-    size_t logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, total;
+    size_t logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, pos_of, y,
+        total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -112,6 +168,9 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     L.h = take(P * I * 4);
     L.q2 = take(P * I);
     L.s2 = take(P * 4);
+    const bool chunk = M > kMaxGemvTokens;
+    L.pos_of = take(chunk ? P * 4 : 0);
+    L.y = take(chunk ? P * (size_t)H * 4 : 0);
     L.total = off;
     return L;
 }
@@ -137,5 +196,17 @@ hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 const char* kernel_names(int H, int I, int mt);
+
+// Chunk-path launchers (moe_chunk.hip).  S is the slot bound min(E, M*K).
+bool chunk_shape_supported(int H, int I, int E);
+hipError_t launch_chunk_router(int H, const ChunkRouterArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_chunk_topk(const ChunkTopkArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_sort_pairs(const SortArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_chunk_gate_up(int H, int I, int S, const ChunkGateUpArgs& a, hipStream_t s,
+                                const LaunchEvents& ev = {});
+hipError_t launch_chunk_down(int H, int I, int S, const ChunkDownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_combine(int H, const CombineArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of, int P, int row_bytes, hipStream_t s);
+const char* chunk_kernel_names(int H, int I);
 
 }  // namespace moe

@@ -36,20 +36,23 @@ def _shape(moe, H=2560, I=768, E=256, K=8):
 
 def test_workspace_bytes(moe):
     s = _shape(moe)
-    sizes = [moe.moe_workspace_bytes(s, m) for m in range(1, 9)]
+    sizes = [moe.moe_workspace_bytes(s, m) for m in list(range(1, 10)) + [512, 2048]]
     assert all(b > 0 for b in sizes)
-    assert sizes == sorted(sizes)
+    assert sizes == sorted(sizes)      # a workspace sized for M serves every smaller M
     # h [M*K, I] fp32 alone is 8*768*4 bytes at M=1
     assert sizes[0] >= 8 * 768 * 4
+    # the chunk path also keeps the weighted expert outputs y [M*K, H] fp32
+    assert sizes[-1] >= 2048 * 8 * 2560 * 4
     assert moe.moe_workspace_bytes(s, 0) == 0
-    assert moe.moe_workspace_bytes(s, 9) == 0
+    assert moe.moe_workspace_bytes(s, 2049) == 0
     assert moe.moe_workspace_bytes(_shape(moe, H=512, I=128), 1) == 0
     assert moe.moe_workspace_bytes(_shape(moe, 256, 64, 16, 2), 1) > 0
 
 
 @pytest.mark.parametrize("shape,M,status", [
     ((2560, 768, 256, 8), 0, -1),          # M must be positive
-    ((2560, 768, 256, 8), 9, -2),          # GEMV path compiled up to 8 tokens
+    ((2560, 768, 256, 8), 2049, -2),       # chunk path compiled up to 2048 tokens
+    ((2560, 768, 200, 8), 9, -2),          # chunk path needs E % 16 == 0
     ((2560, 768, 4, 8), 1, -1),            # K > E
     ((2560, 768, 256, 9), 1, -2),          # K above 8
     ((2560, 768, 1024, 8), 1, -2),         # E above 512
@@ -96,3 +99,5 @@ def test_status_strings_and_path_info(moe):
     assert st == 0 and "gate_up_kernel<H=2560,I=768>" in info and "down_kernel" in info
     st, info = moe.moe_path_info(_shape(moe, 256, 64, 16, 2), 4)
     assert st == 0 and "H=256" in info
+    st, info = moe.moe_path_info(_shape(moe), 512)
+    assert st == 0 and info.startswith("chunk path") and "chunk_gate_up_kernel<2560,768>" in info
