@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     p.add_argument("--tokens", type=str, default="1,4", help="token counts to time (the first is the reported value)")
+    p.add_argument("--chunk-tokens", type=int, default=512, help="tokens of the chunk measurement (0: skip)")
+    p.add_argument("--chunk-steps", type=int, default=400, help="timed chunk layer forwards")
     return p.parse_args()
 
 
@@ -210,6 +212,10 @@ def main() -> int:
                       "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9}
         del graphs, xs
 
+    chunk = None
+    if args.chunk_tokens > 0:
+        chunk = chunk_bench(args, moe, synth, stack, shp, stream)
+
     cpu = None
     if args.cpu_layers > 0:
         cpu = cpu_baseline(args.cpu_layers)
@@ -251,17 +257,123 @@ def main() -> int:
                      "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
+        "chunk": chunk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
 
 
+FP4_PEAK_TFLOPS = 10100.0     # dense FP4 matrix peak of the chip
+FP8_PEAK_TFLOPS = 5000.0      # dense FP8 matrix peak (the mixed FP8 x FP4 form is not faster than this)
+
+
+def chunk_bench(args, moe, synth, stack, shp, stream) -> dict:
+    """A chunk of M tokens per layer (Zipf-skewed routing) through the chunk
+    path, over the same cold 40-layer walk."""
+    import numpy as np
+    import torch
+    M, L = args.chunk_tokens, len(stack)
+    # per-layer routers with a popularity bias channel: token channel 0 is 1.0
+    # and expert e's channel-0 weight is tau * (-1.1 * ln rank_e)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    routers, xs = [], []
+    for l in range(L):
+        wr = stack[l]["wr"].view(torch.bfloat16).float()
+        ranks = torch.randperm(E, generator=g, device="cuda").float() + 1.0
+        wr[:, 0] = 0.5 * (-1.1 * torch.log(ranks))
+        routers.append(wr.to(torch.bfloat16).view(torch.uint16).contiguous())
+        x = torch.randn((M, H), generator=g, device="cuda")
+        x[:, 0] = 1.0
+        xs.append(x.to(torch.bfloat16).view(torch.uint16).contiguous())
+    ws = moe.workspace(shp, M)
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    n_active = torch.zeros(L, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            moe.moe_route(shp, M, xs[l], routers[l], ids, wts, ws, taps={"n_active": n_active[l:l + 1]})
+    torch.cuda.synchronize()
+    n_act = n_active.cpu().numpy().astype(np.int64)
+    if n_act.min() < K or n_act.max() > E:
+        raise RuntimeError(f"chunk routing pre-pass read back distinct-expert counts outside [{K}, {E}]")
+    layer_b = [int(n) * EXPERT_BYTES + ROUTER_BYTES + M * H * 2 + M * H * 4 for n in n_act]
+    P = M * K
+    flops_gu = 2.0 * P * (2 * I) * H
+    flops_down = 2.0 * P * H * I
+
+    def fwd(l, events=None):
+        Ly = stack[l]
+        if events is None:
+            moe.moe_decode_forward(shp, M, xs[l], routers[l], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws)
+        else:
+            moe.moe_decode_forward_events(shp, M, xs[l], routers[l], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"],
+                                          out, ws, events)
+
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            fwd(l)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for l in range(L):
+                fwd(l)
+        graph.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, math.ceil(args.chunk_steps / L))
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(n_rep):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    us_layer = ms * 1e3 / (n_rep * L)
+    gbs = n_rep * sum(layer_b) / (ms * 1e-3) / 1e9
+    # per-kernel execution times from launch-stamped events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+    dur = {"router": [], "gate_up": [], "down": []}
+    with torch.cuda.stream(stream):
+        for row in evs:
+            for e in row:
+                e.record(stream)
+        torch.cuda._sleep(50_000_000)
+        for l in range(L):
+            fwd(l, events=evs[l])
+        torch.cuda.synchronize()
+    for l in range(L):
+        for k, name in enumerate(("router", "gate_up", "down")):
+            dur[name].append(evs[l][2 * k].elapsed_time(evs[l][2 * k + 1]))
+    kus = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}
+    gu_bytes = float(np.mean(n_act)) * W13_BYTES
+    dn_bytes = float(np.mean(n_act)) * W2_BYTES
+    mfma_layer = (flops_gu + flops_down) / (us_layer * 1e-6) / 1e12
+    log(f"chunk M={M}: {us_layer:.1f} us/layer, {gbs:.0f} GB/s, experts touched {n_act.mean():.1f}, "
+        f"kernels (us) {kus}, matrix-core {mfma_layer:.1f} TFLOP/s over the layer")
+    return {"tokens": M, "us_per_layer": round(us_layer, 2), "gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "mean_experts_touched": round(float(n_act.mean()), 1),
+            "kernel_us": {k: round(v, 2) for k, v in kus.items()},
+            "gate_up_gbs": round(gu_bytes / (kus["gate_up"] * 1e-6) / 1e9, 1),
+            "down_gbs": round(dn_bytes / (kus["down"] * 1e-6) / 1e9, 1),
+            "mfma": {"flops_per_layer": flops_gu + flops_down,
+                     "tflops_layer": round(mfma_layer, 1),
+                     "tflops_gate_up_kernel": round(flops_gu / (kus["gate_up"] * 1e-6) / 1e12, 1),
+                     "tflops_down_kernel": round(flops_down / (kus["down"] * 1e-6) / 1e12, 1),
+                     "util_vs_fp4_peak": round(mfma_layer / FP4_PEAK_TFLOPS, 4),
+                     "util_vs_fp8_peak": round(mfma_layer / FP8_PEAK_TFLOPS, 4)},
+            "workload": f"{M}-token chunk per layer, Zipf-1.1 routing through a bias channel, cold 40-layer walk, "
+                        "hip graph"}
+
+
 # HBM traffic of the gate/up kernel comes from hardware counters taken with
 # rocprofv3 (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
 # and is only reported while the kernel source is the one it was taken on.
 KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
-                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp"]
+                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp",
+                  "mxfp4_weight_streaming_amd/csrc/topk_wave.hpp"]
 TRAFFIC_FILE = "profiles/gate_up_hbm_traffic.txt"
 
 

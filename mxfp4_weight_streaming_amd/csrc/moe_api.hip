@@ -95,6 +95,11 @@ struct Carved {
         return {at<int32_t>(L.n_act), at<int32_t>(L.act_experts), at<int32_t>(L.offsets),
                 at<int32_t>(L.pair_token), at<int32_t>(L.pair_src)};
     }
+    moe::ChunkList chunks(const moe_shape* s, int32_t M) const
+    {
+        const int P = M * s->topk, S = s->num_experts < P ? s->num_experts : P;
+        return {at<int32_t>(L.n_chunks), at<int4>(L.chunk_rec), moe::chunk_bound(S, P)};
+    }
 };
 
 Carved carve(const moe_shape* s, int32_t M, void* ws)
@@ -182,7 +187,7 @@ moe_status enqueue_chunk_topk(const moe_shape* s, int32_t M, int32_t* ids, float
 
 moe_status enqueue_sort(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st)
 {
-    moe::SortArgs a{ids, M, s->topk, s->num_experts, c.cp(), c.at<int32_t>(c.L.pos_of)};
+    moe::SortArgs a{ids, M, s->topk, s->num_experts, c.cp(), c.at<int32_t>(c.L.pos_of), c.chunks(s, M)};
     hipError_t e = moe::launch_sort_pairs(a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "pair sort launch");
 }
@@ -191,23 +196,26 @@ moe_status enqueue_chunk_gate_up(const moe_shape* s, int32_t M, const uint8_t* a
                                  const uint8_t* w13, const uint8_t* s13, const Carved& c, hipStream_t st,
                                  const moe::LaunchEvents& ev = {})
 {
-    moe::ChunkGateUpArgs a{c.cp(), w13, s13, act_q, act_s, c.at<float>(c.L.h)};
-    hipError_t e = moe::launch_chunk_gate_up(s->hidden, s->inter, num_slots(s, M), a, st, ev);
+    moe::ChunkGateUpArgs a{c.cp(), c.chunks(s, M), w13, s13, act_q, act_s, c.at<float>(c.L.h)};
+    hipError_t e = moe::launch_chunk_gate_up(s->hidden, s->inter, moe::chunk_bound(num_slots(s, M), M * s->topk), a,
+                                             st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk gate_up launch");
 }
 
 moe_status enqueue_chunk_down(const moe_shape* s, int32_t M, const uint8_t* q2, const float* s2, bool by_pair,
-                              const float* topk_w, const uint8_t* w2, const uint8_t* sw2, const Carved& c,
-                              hipStream_t st, const moe::LaunchEvents& ev = {})
+                              const uint8_t* w2, const uint8_t* sw2, const Carved& c, hipStream_t st,
+                              const moe::LaunchEvents& ev = {})
 {
-    moe::ChunkDownArgs a{c.cp(), w2, sw2, q2, s2, by_pair ? 1 : 0, topk_w, c.at<float>(c.L.y)};
-    hipError_t e = moe::launch_chunk_down(s->hidden, s->inter, num_slots(s, M), a, st, ev);
+    moe::ChunkDownArgs a{c.cp(), c.chunks(s, M), w2, sw2, q2, s2, by_pair ? 1 : 0, c.at<float>(c.L.y)};
+    hipError_t e = moe::launch_chunk_down(s->hidden, s->inter, moe::chunk_bound(num_slots(s, M), M * s->topk), a, st,
+                                          ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk down launch");
 }
 
-moe_status enqueue_combine(const moe_shape* s, int32_t M, float* out, const Carved& c, hipStream_t st)
+moe_status enqueue_combine(const moe_shape* s, int32_t M, const float* topk_w, float* out, const Carved& c,
+                           hipStream_t st)
 {
-    moe::CombineArgs a{c.at<float>(c.L.y), c.at<int32_t>(c.L.pos_of), M, s->topk, out};
+    moe::CombineArgs a{c.at<float>(c.L.y), c.at<int32_t>(c.L.pos_of), topk_w, M, s->topk, out};
     hipError_t e = moe::launch_combine(s->hidden, a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
@@ -231,10 +239,10 @@ moe_status enqueue_chunk_experts(const moe_shape* s, int32_t M, const uint8_t* a
     if ((r = enqueue_chunk_gate_up(s, M, act_q, act_s, w13, s13, c, st, ev_gate_up)) != MOE_OK) return r;
     if ((r = enqueue_requant(s, M, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), st)) != MOE_OK)
         return r;
-    if ((r = enqueue_chunk_down(s, M, c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), false, topk_w, w2, sw2, c, st,
+    if ((r = enqueue_chunk_down(s, M, c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), false, w2, sw2, c, st,
                                 ev_down)) != MOE_OK)
         return r;
-    return enqueue_combine(s, M, out, c, st);
+    return enqueue_combine(s, M, topk_w, out, c, st);
 }
 
 moe_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st)
@@ -428,9 +436,9 @@ moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* in
     const Carved c = carve(shape, M, ws);
     if (chunked(M)) {
         if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
-        if ((st = enqueue_chunk_down(shape, M, inter_fp8, inter_scale, true, topk_w, w2, w2_scale, c, s)) != MOE_OK)
+        if ((st = enqueue_chunk_down(shape, M, inter_fp8, inter_scale, true, w2, w2_scale, c, s)) != MOE_OK)
             return st;
-        return enqueue_combine(shape, M, out, c, s);
+        return enqueue_combine(shape, M, topk_w, out, c, s);
     }
     if ((st = enqueue_topk(shape, M, false, topk_ids, nullptr, nullptr, c, s)) != MOE_OK) return st;
     return enqueue_down(shape, M, nullptr, inter_fp8, inter_scale, nullptr, nullptr, topk_w, w2, w2_scale, out, c, s);

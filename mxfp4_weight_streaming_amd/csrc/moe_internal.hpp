@@ -105,15 +105,29 @@ struct ChunkTopkArgs {
     float* w;              // [M,K]
 };
 
+// Work list of the grouped kernels: the sorted rows of each active expert
+// cut into chunks of at most kChunkRows rows, larger chunks first.
+constexpr int kChunkRows = 64;
+
+struct ChunkList {
+    int32_t* n_chunks;     // [1]
+    int4* rec;             // [C] {expert, first sorted position, rows, 0}; rows = 0 past the last chunk
+    int C;                 // entries of rec (chunk_bound)
+};
+
+inline int chunk_bound(int S, int P) { return S + (P + kChunkRows - 1) / kChunkRows; }
+
 struct SortArgs {
     const int32_t* ids;    // [M,K]; out-of-range ids are clamped into [0, E)
     int M, K, E;
     Compaction cp;         // written
     int32_t* pos_of;       // [M*K]
+    ChunkList chunks;      // written
 };
 
 struct ChunkGateUpArgs {
     Compaction cp;         // read
+    ChunkList chunks;      // read
     const uint8_t* w13;    // [E,2I,H/2]
     const uint8_t* s13;    // [E,2I,H/32]
     const uint8_t* act_q;  // [M,H]
@@ -123,18 +137,19 @@ struct ChunkGateUpArgs {
 
 struct ChunkDownArgs {
     Compaction cp;         // read
+    ChunkList chunks;      // read
     const uint8_t* w2;     // [E,H,I/2]
     const uint8_t* sw2;    // [E,H,I/32]
     const uint8_t* q2;     // [M*K,I] E4M3 intermediate
     const float* s2;       // [M*K]
     int by_pair;           // 0: q2/s2 rows in sorted order; 1: in pair order
-    const float* topk_w;   // [M*K] router weights in pair order
-    float* y;              // [M*K,H] weighted expert outputs in sorted order
+    float* y;              // [M*K,H] expert outputs (s2 applied) in sorted order
 };
 
 struct CombineArgs {
     const float* y;        // [M*K,H] sorted order
     const int32_t* pos_of; // [M*K]
+    const float* w;        // [M*K] router weights in pair order
     int M, K;
     float* out;            // [M,H]
 };
@@ -143,7 +158,7 @@ struct CombineArgs {
 // what it later reads.  pos_of and y exist only for the chunk path.
 struct WsLayout {
     size_t logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, pos_of, y,
-        total;
+        n_chunks, chunk_rec, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -171,6 +186,9 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     const bool chunk = M > kMaxGemvTokens;
     L.pos_of = take(chunk ? P * 4 : 0);
     L.y = take(chunk ? P * (size_t)H * 4 : 0);
+    const size_t C = chunk ? (size_t)chunk_bound((int)S, (int)P) : 0;
+    L.n_chunks = take(chunk ? 4 : 0);
+    L.chunk_rec = take(C * 16);
     L.total = off;
     return L;
 }
@@ -197,14 +215,15 @@ hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStr
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 const char* kernel_names(int H, int I, int mt);
 
-// Chunk-path launchers (moe_chunk.hip).  S is the slot bound min(E, M*K).
+// Chunk-path launchers (moe_chunk.hip).
 bool chunk_shape_supported(int H, int I, int E);
 hipError_t launch_chunk_router(int H, const ChunkRouterArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_chunk_topk(const ChunkTopkArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_sort_pairs(const SortArgs& a, hipStream_t s, const LaunchEvents& ev = {});
-hipError_t launch_chunk_gate_up(int H, int I, int S, const ChunkGateUpArgs& a, hipStream_t s,
+// C is the chunk bound chunk_bound(S, M*K).
+hipError_t launch_chunk_gate_up(int H, int I, int C, const ChunkGateUpArgs& a, hipStream_t s,
                                 const LaunchEvents& ev = {});
-hipError_t launch_chunk_down(int H, int I, int S, const ChunkDownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+hipError_t launch_chunk_down(int H, int I, int C, const ChunkDownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_combine(int H, const CombineArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of, int P, int row_bytes, hipStream_t s);
 const char* chunk_kernel_names(int H, int I);

@@ -21,7 +21,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
-                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp"]
+                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp",
+                  "mxfp4_weight_streaming_amd/csrc/topk_wave.hpp"]
 
 
 def kernel_source_hash() -> str:
