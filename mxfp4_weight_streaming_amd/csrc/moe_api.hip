@@ -136,11 +136,10 @@ moe_status enqueue_topk(const moe_shape* s, int32_t M, bool from_logits, const i
 // from caller-given ids.
 moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const int32_t* ids, int32_t* ids_out, float* w_out,
                            const uint8_t* act_q, const float* act_s, const uint8_t* w13, const uint8_t* s13, float* h,
-                           const uint8_t* w2_prefetch, const uint8_t* sw2_prefetch, const Carved& c, hipStream_t st,
-                           const moe::LaunchEvents& ev = {})
+                           const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {})
 {
     const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids};
-    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, w2_prefetch, sw2_prefetch, nullptr};
+    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h};
     hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
 }
@@ -302,9 +301,7 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
         return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2));
     }
     if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, w2, w2_scale, c, s, ev(1))) !=
-        MOE_OK)
-        return st;
+    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, c, s, ev(1))) != MOE_OK) return st;
     return enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s, ev(2));
 }
 
@@ -387,8 +384,8 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M, const uint8_t*
     float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
     uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
     float* s2_tap = taps ? taps->inter_scale : nullptr;
-    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, w2,
-                              w2_scale, c, s)) != MOE_OK)
+    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, c, s)) !=
+        MOE_OK)
         return st;
     return enqueue_down(shape, M, h, nullptr, nullptr, q2_tap, s2_tap, topk_w, w2, w2_scale, out, c, s);
 }
@@ -416,8 +413,8 @@ moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8
         if ((st = gather_out(inter_fp8, c.at<void>(c.L.q2), M, K, I, c, s)) != MOE_OK) return st;
         return gather_out(inter_scale, c.at<void>(c.L.s2), M, K, 4, c, s);
     }
-    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, nullptr,
-                              nullptr, c, s)) != MOE_OK)
+    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, c, s)) !=
+        MOE_OK)
         return st;
     return enqueue_requant(shape, M, h, inter_fp8, inter_scale, s);
 }

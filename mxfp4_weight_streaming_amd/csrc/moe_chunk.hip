@@ -145,11 +145,9 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void chunk_router_kernel(Chun
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
 {
-    __shared__ TopkScratch sc[4];
-    const int w = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + w;
-    if (t >= a.M) return;                              // whole wave; only wave-level syncs follow
-    topk_wave(a.logits + (size_t)t * a.E, a.E, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K, sc[w]);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.M) return;                              // whole wave; no barrier follows
+    topk_wave(a.logits + (size_t)t * a.E, a.E, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K);
 }
 
 // ---------------------------------------------------------------------------

@@ -62,9 +62,6 @@ struct GateUpArgs {
     const uint8_t* act_q;  // [M,H]
     const float* act_s;    // [M]
     float* h;              // [M*K,I]
-    const uint8_t* w2;     // [E,H,I/2] down weights to prefetch, or nullptr
-    const uint8_t* sw2;    // [E,H,I/32]
-    uint32_t* sink;        // never-null only to keep prefetch loads alive; pass nullptr
 };
 
 struct DownArgs {

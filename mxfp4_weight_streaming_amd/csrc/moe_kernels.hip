@@ -13,8 +13,10 @@
 //                   verify touches up to 32 experts), then streams the fused
 //                   gate/up MXFP4 GEMV of (expert, row block) items with the
 //                   SiLU(gate)*up epilogue ([EN] same section, item 1: the
-//                   768-wide expert layer), pulling each expert's
-//                   down-projection weights into the memory-side cache.
+//                   768-wide expert layer).  (Pulling the down weights into
+//                   the memory-side cache here was measured slower: it adds
+//                   their bytes to this kernel's stream for little gain in
+//                   the next.)
 //   down_kernel     requantises the intermediate to FP8 per (token, expert)
 //                   row while its weight loads are in flight, then the down
 //                   GEMV over all selected experts and the router-weighted
@@ -78,7 +80,6 @@ struct alignas(16) RouteLds {
     int32_t offsets[kMaxPairs + 1];
     int32_t pair_token[kMaxPairs];
     int32_t pair_src[kMaxPairs];
-    TopkScratch topk[4];
 };
 
 // One wave; lane p < P owns pair p with expert e_p.  Its compacted position
@@ -148,7 +149,7 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
     const int M = src.M, E = src.E, K = src.K, P = M * K;
     if (src.logits != nullptr) {
         for (int t = wave; t < M; t += nw)
-            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K, r.topk[wave]);
+            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K);
     } else {
         for (int i = tid; i < P; i += blockDim.x) r.ids[i] = min(max(src.ids[i], 0), E - 1);   // clamped, never OOB
     }
@@ -340,15 +341,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 
     // 2. work items (selected expert, block of rows), strided over the grid;
     //    the next item's weight loads are in flight while this one computes
-    constexpr size_t W2C = (size_t)H * I / 2, W2S = (size_t)H * I / 32;     // down bytes per expert
-    constexpr int PFC = (int)(W2C / BPE / 16), PFS = (int)(W2S / BPE / 16);
-    static_assert(W2C % (16 * BPE) == 0 && W2S % (16 * BPE) == 0, "prefetch split");
-    constexpr int PF_PER = (PFC + PFS + 255) / 256;
-
     struct Stage {
         u32x4 wg[CPL], wu[CPL];
         uint32_t sg[CPL], su[CPL];
-        u32x4 pf[PF_PER];
     };
     auto issue = [&](int item, Stage& st) {
         const int slot = item / BPE, rb = item % BPE;
@@ -367,17 +362,6 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
         for (int i = 0; i < CPL; ++i) {
             st.sg[i] = gsc[li + LPR * i];
             st.su[i] = usc[li + LPR * i];
-        }
-        // this item's share of the expert's down-projection weights, pulled
-        // into the memory-side cache for the down kernel
-        if (a.w2 != nullptr) {
-#pragma unroll
-            for (int j = 0; j < PF_PER; ++j) {
-                const int i = threadIdx.x + 256 * j;
-                if (i < PFC) st.pf[j] = *((const u32x4*)(a.w2 + e * W2C) + rb * PFC + i);
-                else if (i < PFC + PFS) st.pf[j] = *((const u32x4*)(a.sw2 + e * W2S) + rb * PFS + (i - PFC));
-                else st.pf[j] = u32x4{0u, 0u, 0u, 0u};
-            }
         }
     };
     auto compute = [&](int item, Stage& st) {
@@ -420,12 +404,6 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
                 const float g = accg[t] * sc, u = accu[t] * sc;
                 if (li == 0) a.h[(size_t)rl.pair_src[p0 + t] * I + r] = g / (1.0f + expf(-g)) * u;
             }
-        }
-        if (a.w2 != nullptr) {           // retire the prefetch loads
-            uint32_t x = 0;
-#pragma unroll
-            for (int j = 0; j < PF_PER; ++j) x ^= st.pf[j].x ^ st.pf[j].y ^ st.pf[j].z ^ st.pf[j].w;
-            if (a.sink != nullptr) a.sink[threadIdx.x] = x;
         }
     };
 
@@ -845,7 +823,7 @@ const char* kernel_names(int H, int I, int mt)
                "per item) -> down_kernel<H=256,I=64> (FP8 requantisation prologue; 2 lanes/row, 32 rows/WG)";
     if (H == 2560 && I == 768)
         return "router_kernel<H=2560> -> gate_up_kernel<H=2560,I=768> (routing prologue; 16 lanes/row, 16 row-pairs "
-               "per item, 48 items/expert, up to 512 WGs, prefetches the down weights) -> down_kernel<H=2560,I=768> "
+               "per item, 48 items/expert, up to 512 WGs) -> down_kernel<H=2560,I=768> "
                "(FP8 requantisation prologue; 8 lanes/row, 8 rows/WG, 320 WGs)";
     return "unsupported";
 }

@@ -27,31 +27,15 @@ __device__ __forceinline__ float f32_from_orderable(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t topk_key(float v, int e)
-{
-    return ((uint64_t)f32_orderable(v + 0.0f) << 32) | (uint32_t)(~(uint32_t)e);   // + 0.0f folds -0 into +0
-}
-
-// Per-wave LDS scratch of the top-K: the selected keys in ascending expert order.
-struct TopkScratch {
-    uint32_t u[kMaxTopK];
-    int32_t e[kMaxTopK];
-};
-
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Top-K of one token's E logits by one wave, as a radix select: 32 steps of
-// ballot counting find T, the K-th largest orderable logit; the selection is
-// every logit above T plus, among those equal to T, the lowest expert
-// indices.  The K winners are then ranked by (logit descending, index
-// ascending) and their weights are the softmax over the selected logits.
+// Top-K of one token's E logits by one wave, as K rounds of a wave-wide
+// maximum of the orderable logit: each round takes the largest remaining
+// value and, among the experts holding it, the lowest index (expert
+// e = lane + 64 i, so the first slot i whose ballot matches, at its lowest
+// lane), so the winners come out in canonical order (logit descending, lower
+// index first among equal logits).  A taken value is cleared to 0, below
+// every real value.  The weights are the softmax over the selected logits.
 template <int PER>
-__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out, TopkScratch& sc)
+__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
     uint32_t u[PER];
@@ -61,88 +45,46 @@ __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, floa
         const float v = L[e < E ? e : E - 1];
         u[i] = (e < E) ? f32_orderable(v + 0.0f) : 0u;   // + 0.0f folds -0 into +0
     }
-    // Radix select of T, the largest value with count(u >= T) >= K.  As soon
-    // as some candidate has exactly K keys at or above it, those K keys are
-    // the selection (every other key is strictly smaller) and the search stops.
-    uint32_t T = 0;
-    bool exact = false;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = T | (1u << b);
-        int cnt = 0;
+    uint32_t my_u = 0u;                         // lane r ends with the rank-r value and expert
+    int my_e = 0;
+    uint32_t top = 0u;
+    for (int r = 0; r < K; ++r) {
+        uint32_t best = u[0];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(u[i] >= cand));
-        if (cnt >= K) {
-            T = cand;
-            if (cnt == K) {
-                exact = true;
-                break;
+        for (int i = 1; i < PER; ++i) best = max(best, u[i]);
+        const uint32_t m = wave_max_u32(best);
+        int wi = PER, wl = 0;
+#pragma unroll
+        for (int i = PER - 1; i >= 0; --i) {    // the lowest slot with a match wins
+            const uint64_t b = __ballot(u[i] == m);
+            if (b != 0ull) {
+                wi = i;
+                wl = (int)__builtin_ctzll(b);
             }
         }
-    }
-    uint64_t sel[PER];
-    if (exact) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) sel[i] = __ballot(u[i] >= T);
-    } else {
-        // T is the K-th largest value: every key above T, then keys equal to T
-        // in ascending expert order (expert = lane + 64 * slot: slot-major)
-        int need = K;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            sel[i] = __ballot(u[i] > T);
-            need -= __popcll(sel[i]);
+        if (r == 0) top = m;
+        if (lane == r) {
+            my_u = m;
+            my_e = wl + kWave * wi;
         }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            uint64_t m = __ballot(u[i] == T);
-            while (need > 0 && m != 0ull) {
-                const uint64_t low = m & (~m + 1ull);
-                sel[i] |= low;
-                m ^= low;
-                --need;
-            }
-        }
+        for (int i = 0; i < PER; ++i) u[i] = (i == wi && lane == wl) ? 0u : u[i];
     }
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if ((sel[i] >> lane) & 1ull) {
-            const int pos = base + __popcll(sel[i] & ((1ull << lane) - 1ull));
-            sc.u[pos] = u[i];
-            sc.e[pos] = lane + kWave * i;
-        }
-        base += __popcll(sel[i]);
-    }
-    wave_lds_sync();
-    // every lane reads all kMaxTopK scratch entries (broadcast, unconditional);
-    // entries at or past K are masked out of the arithmetic
-    const uint32_t uj = sc.u[lane & (kMaxTopK - 1)];
-    const int ej = sc.e[lane & (kMaxTopK - 1)];
-    uint32_t umax = 0;
-    int rank = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        const uint32_t uk = sc.u[k];
-        const int ek = sc.e[k];
-        const bool in = k < K;
-        rank += in && ((uk > uj) || (uk == uj && ek < ej));
-        umax = in ? max(umax, uk) : umax;
-    }
-    const float ex = (lane < K) ? expf(f32_from_orderable(uj) - f32_from_orderable(umax)) : 0.0f;
+    const float lmax = f32_from_orderable(top);
+    const float ex = (lane < K) ? expf(f32_from_orderable(my_u) - lmax) : 0.0f;
     const float den = wave_sum(ex);
     if (lane < K) {
-        ids_out[rank] = ej;
-        w_out[rank] = ex / den;
+        ids_out[lane] = my_e;
+        w_out[lane] = ex / den;
     }
-    wave_lds_sync();   // the scratch may be reused by this wave's next token
 }
 
-__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out, TopkScratch& sc)
+__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out)
 {
-    if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out, sc);
-    else if (E <= 128) topk_wave_t<2>(L, E, K, ids_out, w_out, sc);
-    else if (E <= 256) topk_wave_t<4>(L, E, K, ids_out, w_out, sc);
-    else topk_wave_t<8>(L, E, K, ids_out, w_out, sc);
+    if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out);
+    else if (E <= 128) topk_wave_t<2>(L, E, K, ids_out, w_out);
+    else if (E <= 256) topk_wave_t<4>(L, E, K, ids_out, w_out);
+    else topk_wave_t<8>(L, E, K, ids_out, w_out);
 }
 
 }  // namespace moe
