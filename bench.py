@@ -63,6 +63,7 @@ def parse():
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     p.add_argument("--tokens", type=str, default="1,4", help="token counts to time (the first is the reported value)")
+    p.add_argument("--experts", type=int, default=256, help="routed experts per layer (512 is Ling-3.0-flash's own)")
     p.add_argument("--chunk-tokens", type=int, default=512, help="tokens of the chunk measurement (0: skip)")
     p.add_argument("--chunk-steps", type=int, default=400, help="timed chunk layer forwards")
     return p.parse_args()
@@ -70,6 +71,9 @@ def parse():
 
 def main() -> int:
     args = parse()
+    global E, ROUTER_BYTES
+    E = args.experts
+    ROUTER_BYTES = E * H * 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer is not sharded "
               "across GPUs in this library)", file=sys.stderr)
@@ -231,6 +235,12 @@ def main() -> int:
               "plain_us_per_layer": round(r4["plain_us_per_layer"], 3),
               "kernel_us": {k: round(v, 3) for k, v in kernel_stats[4]["us"].items()},
               "gate_up_gbs": round(kernel_stats[4]["gate_up_gbs"], 1)}
+    by_tokens = {str(M): {"us_per_layer": round(results[M]["us_per_layer"], 3), "gbs": round(results[M]["gbs"], 1),
+                          "pct_of_hbm_peak": round(100 * results[M]["gbs"] / HBM_PEAK_GBS, 2),
+                          "mean_distinct_experts": round(results[M]["mean_distinct_experts"], 2),
+                          "plain_us_per_layer": round(results[M]["plain_us_per_layer"], 3),
+                          "kernel_us": {k: round(v, 3) for k, v in kernel_stats[M]["us"].items()}}
+                 for M in token_counts}
     traffic = measured_traffic()
     line = {
         "metric": "MoE-layer decode us + weight-stream HBM GB/s (% of peak), M=1 and M=4",
@@ -245,13 +255,14 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "mxfp4 x e4m3 -> f32",
         "data": "synthetic",
-        "config": {"workload": "ling-shaped MoE decode layer, 1 token, cold walk over 40 layers",
-                   "hidden": H, "expert_inter": I, "experts": E, "topk": K, "tokens": 1, "layers": L,
-                   "launch": "hip graph per 40-layer walk"},
+        "config": {"workload": f"ling-shaped MoE decode layer, {token_counts[0]} token(s), cold walk over {L} layers",
+                   "hidden": H, "expert_inter": I, "experts": E, "topk": K, "tokens": token_counts[0], "layers": L,
+                   "launch": f"hip graph per {L}-layer walk"},
         "us_per_layer": round(r1["us_per_layer"], 3),
         "pct_of_hbm_peak": round(100 * r1["gbs"] / HBM_PEAK_GBS, 2),
         "plain_launch": {"us_per_layer": round(r1["plain_us_per_layer"], 3), "gbs": round(r1["plain_gbs"], 1)},
         "m4": m4,
+        "by_tokens": by_tokens,
         "kernel_us": {k: round(v, 3) for k, v in k1["us"].items()},
         "roofline": {"kernel": "gate_up_kernel<H=2560,I=768> (1 token)", "bound": "hbm",
                      "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
