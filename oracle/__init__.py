@@ -74,6 +74,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_requant.argtypes = [_I, _I, _P, _P, _P]
     L.orc_down_combine.restype = None
     L.orc_down_combine.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    L.orc_lm_head_quant.restype = None
+    L.orc_lm_head_quant.argtypes = [_I, _I, _P, _P, _P]
+    L.orc_lm_head_gemv.restype = None
+    L.orc_lm_head_gemv.argtypes = [_I, _I, _I, _P, _P, _P, _P]
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -234,3 +238,27 @@ def moe_layer(x, wr, w13, s13, w2, sc2, K: int) -> LayerTaps:
     q2, s2 = requant(h)
     out = down_combine(q2, s2, r.ids, r.w, w2, sc2, H)
     return LayerTaps(r, q, s, h, q2, s2, out)
+
+
+def lm_head_quant(w: np.ndarray):
+    """Load-time FP8 quantisation of a bf16 LM head [V,H]: codes [V,H] and one
+    binary32 scale per row (the activation scheme applied to weight rows)."""
+    w = _c(w, np.uint16)
+    V, H = w.shape
+    q = np.zeros((V, H), np.uint8)
+    s = np.zeros(V, np.float32)
+    lib().orc_lm_head_quant(V, H, _ptr(w), _ptr(q), _ptr(s))
+    return q, s
+
+
+def lm_head_gemv(x: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """logits [M,V] = s_v * sum_k E4M3(q[v,k]) * x[t,k], in double."""
+    x = _c(x, np.uint16)
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    M, H = x.shape
+    V = q.shape[0]
+    out = np.zeros((M, V), np.float64)
+    lib().orc_lm_head_gemv(M, V, H, _ptr(x), _ptr(q), _ptr(s), _ptr(out))
+    return out
+

@@ -329,3 +329,34 @@ void orc_moe_layer(int M, int H, int I, int E, int K,
     orc_requant(M * K, I, h, q2, s2);
     orc_down_combine(M, H, I, K, q2, s2, ids, w, w2, sc2, out);
 }
+
+/* ------------------------------------------------------------------------- */
+/* FP8 LM head                                                               */
+/* ------------------------------------------------------------------------- */
+
+/* The output projection (hidden 2,560 -> vocabulary 157,184) is stored in
+ * BF16 and read in full for every generated token; quantising it once to FP8
+ * at load time halves those reads ([EN] "What are the 3 optimizations?",
+ * item 2; [ZH] "三项优化分别做了什么").  The pages fix neither the scale
+ * granularity nor whether the activations are quantised too.  Reading taken:
+ * one binary32 scale per output row, s_v = amax_k |W[v,k]| / 448 (1 for an
+ * all-zero row), codes E4M3(W[v,k] / s_v) -- the activation scheme of
+ * orc_quant_act applied to each weight row -- while the activations stay
+ * BF16 (the saving is in the weight reads).
+ *   logits[t,v] = s_v * sum_k E4M3(q[v,k]) * x[t,k]          (in double) */
+void orc_lm_head_quant(int V, int H, const uint16_t* w, uint8_t* q, float* s)
+{
+    orc_quant_act(V, H, w, q, s);
+}
+
+void orc_lm_head_gemv(int M, int V, int H, const uint16_t* x, const uint8_t* q, const float* s, double* logits)
+{
+    for (int t = 0; t < M; ++t) {
+        for (int v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int k = 0; k < H; ++k)
+                acc += orc_e4m3_value(q[(int64_t)v * H + k]) * (double)bf16_to_float(x[(int64_t)t * H + k]);
+            logits[(int64_t)t * V + v] = (double)s[v] * acc;
+        }
+    }
+}

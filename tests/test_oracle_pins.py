@@ -441,3 +441,56 @@ def test_verify_router_construction_hits_distinct_counts():
         r = oracle.route(li.x, li.wts.wr, 8)
         assert len(set(r.ids.ravel().tolist())) == distinct
         assert r.gap.min() > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# FP8 LM head: load-time row quantisation and the FP8-weight GEMV
+# ---------------------------------------------------------------------------
+def _torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Decode with torch's float8_e4m3fn (a decoder independent of the oracle)."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_lm_head_quant_hand_row():
+    # amax 448 gives scale 1: 448 -> 0x7E, -224 = -1.75*2^7 -> 0xF6, 1 -> 0x38, 0 -> 0
+    row = np.zeros((2, 16), np.float32)
+    row[0, :4] = [448.0, -224.0, 1.0, 0.0]
+    row[1, :4] = [448.0 * 2 ** -10, -224.0 * 2 ** -10, 2 ** -10, 0.0]   # same codes, scale 2^-10
+    q, s = oracle.lm_head_quant(synth.bf16_from_f32(row))
+    assert s[0] == np.float32(1.0) and s[1] == np.float32(2.0 ** -10)
+    assert q[0, :4].tolist() == [0x7E, 0xF6, 0x38, 0x00] and q[1, :4].tolist() == q[0, :4].tolist()
+    assert np.all(q[:, 4:] == 0)
+    qz, sz = oracle.lm_head_quant(np.zeros((1, 8), np.uint16))
+    assert sz[0] == 1.0 and np.all(qz == 0)
+
+
+def test_lm_head_quant_error_bound():
+    """Each dequantised weight is within half an E4M3 step of the bf16 weight
+    (relative 2^-4 for normal codes, 2^-10 * s absolute for subnormals)."""
+    rng = np.random.default_rng(5)
+    w = synth.normal_bf16(rng, (64, 256), 0.02)
+    q, s = oracle.lm_head_quant(w)
+    wf = synth.bf16_to_f32(w).astype(np.float64)
+    deq = _torch_e4m3(q) * s[:, None].astype(np.float64)
+    bound = np.maximum(np.abs(wf) * 2.0 ** -4, s[:, None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(np.abs(deq - wf) <= bound * (1 + 1e-12))
+    assert np.allclose(s, np.abs(wf).max(axis=1).astype(np.float32) / np.float32(448.0), rtol=0, atol=0)
+
+
+def test_lm_head_gemv_one_hot_and_ones():
+    rng = np.random.default_rng(6)
+    V, H = 40, 64
+    q = rng.integers(0, 256, (V, H), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x30
+    s = (2.0 ** rng.uniform(-12, -4, V)).astype(np.float32)
+    for k in (0, 17, 63):
+        x = np.zeros((1, H), np.float32)
+        x[0, k] = 1.0
+        got = oracle.lm_head_gemv(synth.bf16_from_f32(x), q, s)
+        assert np.array_equal(got[0], s.astype(np.float64) * _torch_e4m3(q[:, k]))
+    ones = synth.bf16_from_f32(np.ones((1, H), np.float32))
+    got = oracle.lm_head_gemv(ones, q, s)
+    assert np.allclose(got[0], s.astype(np.float64) * _torch_e4m3(q).sum(axis=1), rtol=1e-15, atol=0)
+    x = synth.normal_bf16(rng, (3, H), 1.0)
+    x2 = synth.bf16_from_f32(2.0 * synth.bf16_to_f32(x))
+    assert np.array_equal(oracle.lm_head_gemv(x2, q, s), 2.0 * oracle.lm_head_gemv(x, q, s))
