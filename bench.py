@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--experts", type=int, default=256, help="routed experts per layer (512 is Ling-3.0-flash's own)")
     p.add_argument("--chunk-tokens", type=int, default=512, help="tokens of the chunk measurement (0: skip)")
     p.add_argument("--chunk-steps", type=int, default=400, help="timed chunk layer forwards")
+    p.add_argument("--lm-head-vocab", type=int, default=157184, help="vocabulary of the FP8 LM-head GEMV (0: skip)")
+    p.add_argument("--lm-head-steps", type=int, default=400, help="timed LM-head GEMV calls per token count")
     return p.parse_args()
 
 
@@ -216,6 +218,10 @@ def main() -> int:
                       "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9}
         del graphs, xs
 
+    lm_head = None
+    if args.lm_head_vocab > 0:
+        lm_head = lm_head_bench(args, moe, stream)
+
     chunk = None
     if args.chunk_tokens > 0:
         chunk = chunk_bench(args, moe, synth, stack, shp, stream)
@@ -269,10 +275,62 @@ def main() -> int:
                      "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
         "chunk": chunk,
+        "lm_head": lm_head,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def lm_head_bench(args, moe, stream) -> dict:
+    """The FP8 LM head (vocabulary x 2560, quantised once from bf16): GEMV
+    time per call at 1 and 4 tokens, alternating between two quantised copies
+    (together above the memory-side cache) so every call streams cold rows."""
+    import torch
+    V = args.lm_head_vocab
+    g = torch.Generator(device="cuda")
+    g.manual_seed(777)
+    copies = []
+    for _ in range(2):
+        w = (torch.randn((V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+        q = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(V, dtype=torch.float32, device="cuda")
+        moe.moe_lm_head_quantize(w, q, sc)
+        torch.cuda.synchronize()
+        del w
+        copies.append((q, sc))
+    res = {}
+    for M in (1, 4):
+        x = (torch.randn((M, H), generator=g, device="cuda")).to(torch.bfloat16).view(torch.int16)
+        logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(stream):
+            for i in range(20):
+                q, sc = copies[i % 2]
+                moe.moe_lm_head_forward(x, q, sc, logits)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(2):
+                    q, sc = copies[i]
+                    moe.moe_lm_head_forward(x, q, sc, logits)
+            graph.replay()
+            torch.cuda.synchronize()
+            n = max(1, args.lm_head_steps // 2)
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(n):
+                graph.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (2 * n)
+        nbytes = V * H + V * 4 + M * H * 2 + M * V * 4
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[str(M)] = {"us_per_call": round(us, 2), "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        log(f"lm head V={V} M={M}: {us:.1f} us per call, {gbs:.0f} GB/s")
+    bf16_bytes = V * H * 2
+    return {"vocab": V, "hidden": H, "by_tokens": res,
+            "weight_bytes_fp8": V * H, "weight_bytes_bf16": bf16_bytes,
+            "workload": "FP8 LM-head GEMV (per-row fp32 scales, bf16 activations), two quantised copies alternated"}
 
 
 FP4_PEAK_TFLOPS = 10100.0     # dense FP4 matrix peak of the chip

@@ -199,6 +199,32 @@ moe_status moe_down_combine(const moe_shape* shape, int32_t M,
  * exhaustive checks of the encoder. */
 moe_status moe_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* q, void* stream);
 
+/* ---- FP8 LM head ----------------------------------------------------------
+ * The output projection (hidden 2,560 -> vocabulary 157,184 on the pages) is
+ * stored in BF16 and read in full for every token; it is quantised to FP8
+ * once at load time so that those reads halve ([EN] "What are the 3
+ * optimizations?", item 2).  Reading taken: one fp32 scale per vocabulary row,
+ * s_v = amax_k |W[v,k]| / 448 (1 for an all-zero row), codes
+ * E4M3_RNE_sat(W[v,k] / s_v) (correctly rounded fp32 divisions: the
+ * activation scheme of moe_quant_act applied to weight rows); activations stay
+ * bf16. */
+
+/* Load-time quantisation.  w_bf16 [vocab, hidden] row-major (16-byte
+ * aligned); q [vocab, hidden] E4M3 codes (16-byte aligned); scale [vocab].
+ * hidden % 8 == 0.  Any vocab > 0.  Caller-owned device memory; asynchronous
+ * on `stream`; nothing is enqueued on an error. */
+moe_status moe_lm_head_quantize(const uint16_t* w_bf16, int32_t vocab, int32_t hidden,
+                                uint8_t* q, float* scale, void* stream);
+
+/* Decode GEMV over the FP8 rows: logits[t, v] = scale[v] * sum_k
+ * E4M3(q[v,k]) * x[t,k], fp32 accumulation of exact products, for M = 1..8
+ * tokens.  x_bf16 [M, hidden] (16-byte aligned); logits [M, vocab] fp32,
+ * overwritten.  Compiled hidden sizes: 512 and 2560 (others return
+ * MOE_ERR_UNSUPPORTED_SHAPE); any vocab > 0. */
+moe_status moe_lm_head_forward(const uint16_t* x_bf16, int32_t M, const uint8_t* q,
+                               const float* scale, int32_t vocab, int32_t hidden,
+                               float* logits, void* stream);
+
 /* Writes a one-line description of the kernels a call with this shape and M
  * would run (NUL-terminated, truncated to len).  Returns the same status the
  * call's shape validation would. */

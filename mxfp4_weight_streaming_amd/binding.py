@@ -67,6 +67,8 @@ _SIGNATURES = {
     "moe_gate_up": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
     "moe_down_combine": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
     "moe_fp8_encode_range": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_int64, _V, _V]),
+    "moe_lm_head_quantize": (ctypes.c_int, [_V, _i32, _i32, _V, _V, _V]),
+    "moe_lm_head_forward": (ctypes.c_int, [_V, _i32, _V, _V, _i32, _i32, _V, _V]),
     "moe_path_info": (ctypes.c_int, [_S, _i32, ctypes.c_char_p, _sz]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -202,6 +204,20 @@ def moe_down_combine(shp, M, inter_fp8, inter_scale, topk_ids, topk_w, w2, w2_sc
 
 def moe_fp8_encode_range(first_bits: int, n: int, q, stream=None):
     _check(_lib.moe_fp8_encode_range(first_bits & 0xFFFFFFFF, n, _p(q), _stream(stream)), "moe_fp8_encode_range")
+
+
+def moe_lm_head_quantize(w_bf16, q, scale, stream=None):
+    """w_bf16 [V,H] -> q [V,H] E4M3 codes and scale [V] (one fp32 scale per row)."""
+    V, H = w_bf16.shape
+    _check(_lib.moe_lm_head_quantize(_p(w_bf16), V, H, _p(q), _p(scale), _stream(stream)), "moe_lm_head_quantize")
+
+
+def moe_lm_head_forward(x_bf16, q, scale, logits, stream=None):
+    """logits [M,V] = scale[v] * sum_k E4M3(q[v,k]) * x[t,k]."""
+    M, H = x_bf16.shape
+    V = q.shape[0]
+    _check(_lib.moe_lm_head_forward(_p(x_bf16), M, _p(q), _p(scale), V, H, _p(logits), _stream(stream)),
+           "moe_lm_head_forward")
 
 
 def moe_path_info(shp: MoeShape, M: int) -> tuple[int, str]:

@@ -441,6 +441,34 @@ moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* in
     return enqueue_down(shape, M, nullptr, inter_fp8, inter_scale, nullptr, nullptr, topk_w, w2, w2_scale, out, c, s);
 }
 
+moe_status moe_lm_head_quantize(const uint16_t* w_bf16, int32_t vocab, int32_t hidden, uint8_t* q, float* scale,
+                                void* stream)
+{
+    CHECK_PTR(w_bf16); CHECK_PTR(q); CHECK_PTR(scale);
+    CHECK_ALIGN(w_bf16); CHECK_ALIGN(q);
+    if (vocab <= 0 || hidden <= 0) return fail(MOE_ERR_INVALID_ARG, "vocab (%d) and hidden (%d) must be positive", vocab, hidden);
+    if (hidden % 8 != 0) return fail(MOE_ERR_INVALID_ARG, "hidden (%d) must be a multiple of 8", hidden);
+    hipError_t e = moe::launch_lm_head_quant(w_bf16, vocab, hidden, q, scale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "lm-head quantisation launch");
+}
+
+moe_status moe_lm_head_forward(const uint16_t* x_bf16, int32_t M, const uint8_t* q, const float* scale,
+                               int32_t vocab, int32_t hidden, float* logits, void* stream)
+{
+    CHECK_PTR(x_bf16); CHECK_PTR(q); CHECK_PTR(scale); CHECK_PTR(logits);
+    CHECK_ALIGN(x_bf16); CHECK_ALIGN(q);
+    if (vocab <= 0) return fail(MOE_ERR_INVALID_ARG, "vocab (%d) must be positive", vocab);
+    if (M <= 0) return fail(MOE_ERR_INVALID_ARG, "M (%d) must be positive", M);
+    if (M > moe::kMaxGemvTokens)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "the LM-head GEMV is compiled for up to %d tokens (M=%d)",
+                    moe::kMaxGemvTokens, M);
+    if (!moe::lm_head_shape_supported(hidden))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d is not a compiled LM-head shape; compiled: 512, 2560", hidden);
+    hipError_t e = moe::launch_lm_head_gemv(hidden, token_bound(M), x_bf16, M, q, scale, vocab, logits,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "lm-head GEMV launch");
+}
+
 moe_status moe_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* q, void* stream)
 {
     if (q == nullptr) return fail(MOE_ERR_INVALID_ARG, "q is NULL");

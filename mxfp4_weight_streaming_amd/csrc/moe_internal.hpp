@@ -225,4 +225,10 @@ hipError_t launch_combine(int H, const CombineArgs& a, hipStream_t s, const Laun
 hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of, int P, int row_bytes, hipStream_t s);
 const char* chunk_kernel_names(int H, int I);
 
+// FP8 LM head (lm_head.hip).  mt is the token bound (1, 2, 4 or 8).
+bool lm_head_shape_supported(int H);
+hipError_t launch_lm_head_quant(const uint16_t* w, int V, int H, uint8_t* q, float* scale, hipStream_t s);
+hipError_t launch_lm_head_gemv(int H, int mt, const uint16_t* x, int M, const uint8_t* q, const float* scale, int V,
+                               float* logits, hipStream_t s);
+
 }  // namespace moe

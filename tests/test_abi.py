@@ -101,3 +101,15 @@ def test_status_strings_and_path_info(moe):
     assert st == 0 and "H=256" in info
     st, info = moe.moe_path_info(_shape(moe), 512)
     assert st == 0 and info.startswith("chunk path") and "chunk_gate_up_kernel<2560,768>" in info
+
+
+def test_lm_head_validation(moe):
+    L = moe.raw()
+    a = 1 << 20
+    assert L.moe_lm_head_quantize(None, 16, 512, a, a, None) == -1
+    assert L.moe_lm_head_quantize(a, 16, 500, a, a, None) == -1          # hidden % 8
+    assert L.moe_lm_head_quantize(a + 2, 16, 512, a, a, None) == -3      # alignment
+    assert L.moe_lm_head_forward(a, 1, a, a, 16, 1024, a, None) == -2     # hidden not compiled
+    assert L.moe_lm_head_forward(a, 9, a, a, 16, 2560, a, None) == -2     # above 8 tokens
+    assert L.moe_lm_head_forward(a, 0, a, a, 16, 2560, a, None) == -1
+    assert L.moe_lm_head_forward(a, 1, a, None, 16, 2560, a, None) == -1
