@@ -227,8 +227,25 @@ class LayerTaps:
         return self.route.gap < 1e-4
 
 
-def moe_layer(x, wr, w13, s13, w2, sc2, K: int) -> LayerTaps:
-    """The whole layer, stage by stage, returning every tap."""
+@dataclass
+class SharedExpert:
+    """One dense MXFP4 expert applied to every token: w13 [2I,H/2], s13 [2I,H/32],
+    w2 [H,I/2], s2 [H,I/32] (one expert of the routed layout)."""
+    w13: np.ndarray
+    s13: np.ndarray
+    w2: np.ndarray
+    s2: np.ndarray
+
+
+def moe_layer(x, wr, w13, s13, w2, sc2, K: int, shared: SharedExpert | None = None) -> LayerTaps:
+    """The whole layer, stage by stage, returning every tap.
+
+    With a shared expert ([EN] "What is Ling 3.0, and why does it suit DGX
+    Spark?": one shared expert per MoE layer beside the 8 routed ones) every
+    token also goes through that expert with weight 1, by the same W4A8 steps
+    (the token's FP8 activations, gate/up + SiLU, its own per-row FP8
+    requantisation, down), and the result is added to the routed sum.  Its rows
+    of h, q2 and s2 follow the M*K routed pairs (row M*K + t for token t)."""
     x = _c(x, np.uint16)
     M, H = x.shape
     I = w2.shape[2] * 2
@@ -237,6 +254,12 @@ def moe_layer(x, wr, w13, s13, w2, sc2, K: int) -> LayerTaps:
     h = gate_up(q, s, r.ids, w13, s13, I)
     q2, s2 = requant(h)
     out = down_combine(q2, s2, r.ids, r.w, w2, sc2, H)
+    if shared is not None:
+        zero = np.zeros((M, 1), np.int32)
+        hs = gate_up(q, s, zero, shared.w13[None], shared.s13[None], I)
+        q2s, s2s = requant(hs)
+        out = out + down_combine(q2s, s2s, zero, np.ones((M, 1)), shared.w2[None], shared.s2[None], H)
+        h, q2, s2 = np.vstack([h, hs]), np.vstack([q2, q2s]), np.concatenate([s2, s2s])
     return LayerTaps(r, q, s, h, q2, s2, out)
 
 

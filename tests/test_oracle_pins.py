@@ -494,3 +494,44 @@ def test_lm_head_gemv_one_hot_and_ones():
     x = synth.normal_bf16(rng, (3, H), 1.0)
     x2 = synth.bf16_from_f32(2.0 * synth.bf16_to_f32(x))
     assert np.array_equal(oracle.lm_head_gemv(x2, q, s), 2.0 * oracle.lm_head_gemv(x, q, s))
+
+
+# ---------------------------------------------------------------------------
+# Shared expert
+# ---------------------------------------------------------------------------
+def _shared_from(w: synth.Weights, e: int) -> oracle.SharedExpert:
+    return oracle.SharedExpert(w.w13[e].copy(), w.s13[e].copy(), w.w2[e].copy(), w.s2[e].copy())
+
+
+def test_shared_expert_equals_top1_routing_to_that_expert():
+    """A shared expert with expert j's weights adds exactly what a K=1 layer
+    that routes every token to j (weight 1) produces."""
+    w = synth.expert_weights(41, 256, 64, 16)
+    rng = np.random.default_rng(42)
+    xf = synth.bf16_to_f32(synth.normal_bf16(rng, (5, 256), 1.0))
+    xf[:, 0] = 1.0
+    x = synth.bf16_from_f32(xf)
+    j = 9
+    wr1 = synth.bf16_to_f32(w.wr).copy()
+    wr1[:, 0] = -40.0
+    wr1[j, 0] = 40.0
+    top1 = oracle.moe_layer(x, synth.bf16_from_f32(wr1), w.w13, w.s13, w.w2, w.s2, 1)
+    assert np.all(top1.route.ids[:, 0] == j) and np.all(top1.route.w == 1.0)
+    base = oracle.moe_layer(x, w.wr, w.w13, w.s13, w.w2, w.s2, 2)
+    with_shared = oracle.moe_layer(x, w.wr, w.w13, w.s13, w.w2, w.s2, 2, shared=_shared_from(w, j))
+    np.testing.assert_allclose(with_shared.out - base.out, top1.out, rtol=1e-12, atol=1e-12 * np.abs(top1.out).max())
+    assert with_shared.h.shape[0] == 5 * 2 + 5
+    np.testing.assert_array_equal(with_shared.q2[10:], top1.q2)
+
+
+def test_shared_expert_zero_down_and_scale_doubling():
+    w = synth.expert_weights(43, 256, 64, 16)
+    li = synth.decode_tokens(44, w, 3, K=2)
+    base = oracle.moe_layer(li.x, w.wr, w.w13, w.s13, w.w2, w.s2, 2)
+    sh = _shared_from(w, 3)
+    sh0 = oracle.SharedExpert(sh.w13, sh.s13, np.zeros_like(sh.w2), sh.s2)
+    np.testing.assert_array_equal(oracle.moe_layer(li.x, w.wr, w.w13, w.s13, w.w2, w.s2, 2, shared=sh0).out, base.out)
+    one = oracle.moe_layer(li.x, w.wr, w.w13, w.s13, w.w2, w.s2, 2, shared=sh).out - base.out
+    sh2 = oracle.SharedExpert(sh.w13, sh.s13, sh.w2, (sh.s2.astype(np.int32) + 1).astype(np.uint8))
+    two = oracle.moe_layer(li.x, w.wr, w.w13, w.s13, w.w2, w.s2, 2, shared=sh2).out - base.out
+    np.testing.assert_allclose(two, 2.0 * one, rtol=1e-12, atol=1e-12 * np.abs(one).max())
