@@ -28,7 +28,14 @@
  *     s2[p] = max|h[p]| / 448 (1 if 0); q2[p] = E4M3_RNE_satfinite(h[p] / s2[p])
  *   out[t] = sum_j w[t,j] * s2[p] * (W2[e] times E4M3(q2[p]))   (fp32, overwritten)
  * where an MXFP4 matrix element is E2M1(code) * 2^(E8M0 block scale - 127).
- * No residual and no shared expert are added.
+ * No residual is added.  The *_shared entry points add the model's shared
+ * expert: each Ling MoE layer sends every token to one shared expert besides
+ * its 8 routed ones ([EN] "What is Ling 3.0, and why does it suit DGX
+ * Spark?").  It is one more expert of the routed layout, taken by every token
+ * with weight 1 through the same steps (gate/up on E4M3(q[t]) * s[t], SiLU*up,
+ * FP8 requantisation, down); its term is added after the K routed terms:
+ *   out[t] = sum_j w[t,j] * y[t*K+j] + y_shared[t]
+ * and its intermediate is row M*K + t of the tapped intermediates.
  *
  * Storage layout (every tensor dense, row-major, no padding):
  *   hidden      bf16 bits  [M, H]
@@ -114,10 +121,20 @@ typedef struct {
     float*   inter_scale;  /* [M*K] fp32 intermediate scale                           */
 } moe_expert_taps;
 
+/* The shared expert: one expert of the routed layout (no leading E axis).
+ * All four pointers are device memory owned by the caller; w13 and w2 must be
+ * 16-byte aligned. */
+typedef struct {
+    const uint8_t* w13;        /* [2I, H/2]  E2M1 codes, rows [0,I) gate, [I,2I) up */
+    const uint8_t* w13_scale;  /* [2I, H/32] E8M0                                    */
+    const uint8_t* w2;         /* [H, I/2]   E2M1 codes                              */
+    const uint8_t* w2_scale;   /* [H, I/32]  E8M0                                    */
+} moe_shared_expert;
+
 /* Bytes of workspace needed for calls with up to max_tokens tokens; 0 if the
  * shape or max_tokens is invalid or unsupported.  The requirement is
  * non-decreasing in max_tokens, so one workspace sized for max_tokens serves
- * every smaller M. */
+ * every smaller M, with or without a shared expert. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens);
 
 /* Zero the workspace (a fill kernel on `stream`; the caller orders later
@@ -148,6 +165,20 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M,
                                      float* out, void* ws, size_t ws_bytes, void* stream,
                                      void* const* events);
 
+/* moe_decode_forward_events plus the shared expert (see the layer definition
+ * above).  `shared` may be NULL: then this is moe_decode_forward_events.
+ * Its slot runs in the same gate/up and down kernels as the routed experts
+ * (after them in slot order), so the layer stays three kernels at M <= 8.
+ * MOE_ERR_INVALID_ARG if a member of *shared is NULL, MOE_ERR_ALIGNMENT if
+ * its w13 or w2 is not 16-byte aligned. */
+moe_status moe_decode_forward_shared(const moe_shape* shape, int32_t M,
+                                     const uint16_t* hidden, const uint16_t* router_w,
+                                     const uint8_t* w13, const uint8_t* w13_scale,
+                                     const uint8_t* w2, const uint8_t* w2_scale,
+                                     const moe_shared_expert* shared,
+                                     float* out, void* ws, size_t ws_bytes, void* stream,
+                                     void* const* events);
+
 /* Router, top-K, renormalised weights and compaction (the first kernel of
  * moe_decode_forward; it also quantises the activations when the taps ask
  * for them).  topk_ids/topk_w [M,K] are written in canonical order (logit
@@ -173,6 +204,18 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M,
                                const uint8_t* w2, const uint8_t* w2_scale,
                                float* out, const moe_expert_taps* taps,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* moe_experts_forward plus the shared expert (`shared` may be NULL).  With a
+ * shared expert the taps hold M*K + M rows: the M*K routed pairs, then the
+ * shared expert's row for token t at M*K + t. */
+moe_status moe_experts_forward_shared(const moe_shape* shape, int32_t M,
+                                      const uint8_t* act_fp8, const float* act_scale,
+                                      const int32_t* topk_ids, const float* topk_w,
+                                      const uint8_t* w13, const uint8_t* w13_scale,
+                                      const uint8_t* w2, const uint8_t* w2_scale,
+                                      const moe_shared_expert* shared,
+                                      float* out, const moe_expert_taps* taps,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 /* Compaction and the fused gate/up kernel, then the per-(token, expert) FP8
  * requantisation as a kernel of its own (moe_decode_forward does the same

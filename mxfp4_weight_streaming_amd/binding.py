@@ -49,8 +49,14 @@ class MoeExpertTaps(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("inter_fp8", ctypes.c_void_p), ("inter_scale", ctypes.c_void_p)]
 
 
+class MoeSharedExpert(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p)]
+
+
 _V = ctypes.c_void_p
 _S = ctypes.POINTER(MoeShape)
+_SH = ctypes.POINTER(MoeSharedExpert)
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 
@@ -60,10 +66,14 @@ _SIGNATURES = {
     "moe_decode_forward": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
     "moe_decode_forward_events": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V,
                                                   ctypes.POINTER(ctypes.c_void_p)]),
+    "moe_decode_forward_shared": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _SH, _V, _V, _sz, _V,
+                                                  ctypes.POINTER(ctypes.c_void_p)]),
     "moe_route": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, ctypes.POINTER(MoeRouteTaps), _V, _sz, _V]),
     "moe_quant_act": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V]),
     "moe_experts_forward": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                            ctypes.POINTER(MoeExpertTaps), _V, _sz, _V]),
+    "moe_experts_forward_shared": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _SH, _V,
+                                                  ctypes.POINTER(MoeExpertTaps), _V, _sz, _V]),
     "moe_gate_up": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
     "moe_down_combine": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _sz, _V]),
     "moe_fp8_encode_range": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_int64, _V, _V]),
@@ -163,6 +173,34 @@ def moe_decode_forward_events(shp, M, hidden, router_w, w13, w13_scale, w2, w2_s
            "moe_decode_forward_events")
 
 
+def _shared(shared):
+    """A MoeSharedExpert from (w13, w13_scale, w2, w2_scale) tensors, or None."""
+    if shared is None:
+        return None
+    if len(shared) != 4:
+        raise ValueError("a shared expert is (w13, w13_scale, w2, w2_scale)")
+    return MoeSharedExpert(*[_p(t) for t in shared])
+
+
+def _events(events):
+    if events is None:
+        return None
+    if len(events) != 6:
+        raise ValueError("events: 6 torch.cuda.Event (start/stop of 3 kernels)")
+    return (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
+
+
+def moe_decode_forward_shared(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, shared, out, ws,
+                              events=None, stream=None):
+    """moe_decode_forward plus the shared expert; shared = (w13, w13_scale, w2,
+    w2_scale) of one expert, or None.  events as in moe_decode_forward_events."""
+    sh = _shared(shared)
+    _check(_lib.moe_decode_forward_shared(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
+                                          _p(w2), _p(w2_scale), ctypes.byref(sh) if sh is not None else None,
+                                          _p(out), _p(ws), _nbytes(ws), _stream(stream), _events(events)),
+           "moe_decode_forward_shared")
+
+
 def moe_route(shp, M, hidden, router_w, topk_ids, topk_w, ws, taps: dict | None = None, stream=None):
     t = None
     if taps is not None:
@@ -187,6 +225,21 @@ def moe_experts_forward(shp, M, act_fp8, act_scale, topk_ids, topk_w, w13, w13_s
                                     ctypes.byref(t) if t is not None else None, _p(ws), _nbytes(ws),
                                     _stream(stream)),
            "moe_experts_forward")
+
+
+def moe_experts_forward_shared(shp, M, act_fp8, act_scale, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, shared,
+                               out, ws, taps: dict | None = None, stream=None):
+    """moe_experts_forward plus the shared expert; taps then hold M*K + M rows."""
+    t = None
+    if taps is not None:
+        t = MoeExpertTaps(*[_p(taps.get(k)) for k, _ in MoeExpertTaps._fields_])
+    sh = _shared(shared)
+    _check(_lib.moe_experts_forward_shared(ctypes.byref(shp), M, _p(act_fp8), _p(act_scale), _p(topk_ids),
+                                           _p(topk_w), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
+                                           ctypes.byref(sh) if sh is not None else None, _p(out),
+                                           ctypes.byref(t) if t is not None else None, _p(ws), _nbytes(ws),
+                                           _stream(stream)),
+           "moe_experts_forward_shared")
 
 
 def moe_gate_up(shp, M, act_fp8, act_scale, topk_ids, w13, w13_scale, h, inter_fp8, inter_scale, ws, stream=None):

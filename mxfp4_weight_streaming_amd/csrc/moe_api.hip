@@ -95,10 +95,15 @@ struct Carved {
         return {at<int32_t>(L.n_act), at<int32_t>(L.act_experts), at<int32_t>(L.offsets),
                 at<int32_t>(L.pair_token), at<int32_t>(L.pair_src)};
     }
-    moe::ChunkList chunks(const moe_shape* s, int32_t M) const
+    // The chunk list's capacity; with a shared expert, one more slot of M rows.
+    static int chunk_cap(const moe_shape* s, int32_t M, bool shared)
     {
         const int P = M * s->topk, S = s->num_experts < P ? s->num_experts : P;
-        return {at<int32_t>(L.n_chunks), at<int4>(L.chunk_rec), moe::chunk_bound(S, P)};
+        return shared ? moe::chunk_bound(S + 1, P + M) : moe::chunk_bound(S, P);
+    }
+    moe::ChunkList chunks(const moe_shape* s, int32_t M, bool shared) const
+    {
+        return {at<int32_t>(L.n_chunks), at<int4>(L.chunk_rec), chunk_cap(s, M, shared)};
     }
 };
 
@@ -111,6 +116,21 @@ int num_slots(const moe_shape* s, int32_t M)
 {
     const int P = M * s->topk;
     return s->num_experts < P ? s->num_experts : P;
+}
+
+// The shared expert's weights as the kernels take them (all null: none).
+moe::SharedWeights shared_weights(const moe_shared_expert* sh)
+{
+    if (sh == nullptr) return {};
+    return {sh->w13, sh->w13_scale, sh->w2, sh->w2_scale};
+}
+
+bool has_shared(const moe::SharedWeights& sh) { return sh.w13 != nullptr; }
+
+// Intermediate rows of a call: M*K routed pairs, then M shared-expert rows.
+int pair_rows(const moe_shape* s, int32_t M, const moe::SharedWeights& sh)
+{
+    return M * s->topk + (has_shared(sh) ? M : 0);
 }
 
 moe_status enqueue_router(const moe_shape* s, int32_t M, const uint16_t* x, const uint16_t* wr, uint8_t* act_q,
@@ -136,17 +156,20 @@ moe_status enqueue_topk(const moe_shape* s, int32_t M, bool from_logits, const i
 // from caller-given ids.
 moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const int32_t* ids, int32_t* ids_out, float* w_out,
                            const uint8_t* act_q, const float* act_s, const uint8_t* w13, const uint8_t* s13, float* h,
-                           const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {})
+                           const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {},
+                           const moe::SharedWeights& sh = {})
 {
-    const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids};
-    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h};
-    hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M), a, st, ev);
+    const int shared = has_shared(sh) ? 1 : 0;
+    const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids,
+                            shared};
+    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, sh};
+    hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M) + shared, a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
 }
 
-moe_status enqueue_requant(const moe_shape* s, int32_t M, const float* h, uint8_t* q2, float* s2, hipStream_t st)
+moe_status enqueue_requant(const moe_shape* s, int32_t rows, const float* h, uint8_t* q2, float* s2, hipStream_t st)
 {
-    moe::RequantArgs a{h, M * s->topk, q2, s2};
+    moe::RequantArgs a{h, rows, q2, s2};
     hipError_t e = moe::launch_requant(s->inter, a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "requant launch");
 }
@@ -155,9 +178,10 @@ moe_status enqueue_requant(const moe_shape* s, int32_t M, const float* h, uint8_
 // caller's E4M3 intermediate q2/s2.
 moe_status enqueue_down(const moe_shape* s, int32_t M, const float* h, const uint8_t* q2, const float* s2,
                         uint8_t* q2_out, float* s2_out, const float* topk_w, const uint8_t* w2, const uint8_t* sw2,
-                        float* out, const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {})
+                        float* out, const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {},
+                        const moe::SharedWeights& sh = {})
 {
-    moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, h, q2, s2, q2_out, s2_out, topk_w, c.cp(), out};
+    moe::DownArgs a{s->num_experts, M, s->topk, w2, sw2, h, q2, s2, q2_out, s2_out, topk_w, c.cp(), out, sh};
     hipError_t e = moe::launch_down(s->hidden, s->inter, token_bound(M), a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
 }
@@ -184,46 +208,48 @@ moe_status enqueue_chunk_topk(const moe_shape* s, int32_t M, int32_t* ids, float
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk topk launch");
 }
 
-moe_status enqueue_sort(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st)
+moe_status enqueue_sort(const moe_shape* s, int32_t M, const int32_t* ids, const Carved& c, hipStream_t st,
+                        bool shared = false)
 {
-    moe::SortArgs a{ids, M, s->topk, s->num_experts, c.cp(), c.at<int32_t>(c.L.pos_of), c.chunks(s, M)};
+    moe::SortArgs a{ids, M, s->topk, s->num_experts, c.cp(), c.at<int32_t>(c.L.pos_of), c.chunks(s, M, shared),
+                    shared ? 1 : 0};
     hipError_t e = moe::launch_sort_pairs(a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "pair sort launch");
 }
 
 moe_status enqueue_chunk_gate_up(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
                                  const uint8_t* w13, const uint8_t* s13, const Carved& c, hipStream_t st,
-                                 const moe::LaunchEvents& ev = {})
+                                 const moe::LaunchEvents& ev = {}, const moe::SharedWeights& sh = {})
 {
-    moe::ChunkGateUpArgs a{c.cp(), c.chunks(s, M), w13, s13, act_q, act_s, c.at<float>(c.L.h)};
-    hipError_t e = moe::launch_chunk_gate_up(s->hidden, s->inter, moe::chunk_bound(num_slots(s, M), M * s->topk), a,
-                                             st, ev);
+    const moe::ChunkList cl = c.chunks(s, M, has_shared(sh));
+    moe::ChunkGateUpArgs a{c.cp(), cl, w13, s13, act_q, act_s, c.at<float>(c.L.h), sh};
+    hipError_t e = moe::launch_chunk_gate_up(s->hidden, s->inter, cl.C, a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk gate_up launch");
 }
 
 moe_status enqueue_chunk_down(const moe_shape* s, int32_t M, const uint8_t* q2, const float* s2, bool by_pair,
                               const uint8_t* w2, const uint8_t* sw2, const Carved& c, hipStream_t st,
-                              const moe::LaunchEvents& ev = {})
+                              const moe::LaunchEvents& ev = {}, const moe::SharedWeights& sh = {})
 {
-    moe::ChunkDownArgs a{c.cp(), c.chunks(s, M), w2, sw2, q2, s2, by_pair ? 1 : 0, c.at<float>(c.L.y)};
-    hipError_t e = moe::launch_chunk_down(s->hidden, s->inter, moe::chunk_bound(num_slots(s, M), M * s->topk), a, st,
-                                          ev);
+    const moe::ChunkList cl = c.chunks(s, M, has_shared(sh));
+    moe::ChunkDownArgs a{c.cp(), cl, w2, sw2, q2, s2, by_pair ? 1 : 0, c.at<float>(c.L.y), sh};
+    hipError_t e = moe::launch_chunk_down(s->hidden, s->inter, cl.C, a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk down launch");
 }
 
 moe_status enqueue_combine(const moe_shape* s, int32_t M, const float* topk_w, float* out, const Carved& c,
-                           hipStream_t st)
+                           hipStream_t st, bool shared = false)
 {
-    moe::CombineArgs a{c.at<float>(c.L.y), c.at<int32_t>(c.L.pos_of), topk_w, M, s->topk, out};
+    moe::CombineArgs a{c.at<float>(c.L.y), c.at<int32_t>(c.L.pos_of), topk_w, M, s->topk, out, shared ? 1 : 0};
     hipError_t e = moe::launch_combine(s->hidden, a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
 // Rows of a sorted-order intermediate, delivered in pair order.
-moe_status gather_out(void* dst, const void* src, int32_t M, int K, int row_bytes, const Carved& c, hipStream_t st)
+moe_status gather_out(void* dst, const void* src, int rows, int row_bytes, const Carved& c, hipStream_t st)
 {
     if (dst == nullptr) return MOE_OK;
-    hipError_t e = moe::launch_gather_rows(src, dst, c.at<int32_t>(c.L.pos_of), M * K, row_bytes, st);
+    hipError_t e = moe::launch_gather_rows(src, dst, c.at<int32_t>(c.L.pos_of), rows, row_bytes, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "tap gather");
 }
 
@@ -232,16 +258,29 @@ moe_status gather_out(void* dst, const void* src, int32_t M, int K, int row_byte
 moe_status enqueue_chunk_experts(const moe_shape* s, int32_t M, const uint8_t* act_q, const float* act_s,
                                  const float* topk_w, const uint8_t* w13, const uint8_t* s13, const uint8_t* w2,
                                  const uint8_t* sw2, float* out, const Carved& c, hipStream_t st,
-                                 const moe::LaunchEvents& ev_gate_up = {}, const moe::LaunchEvents& ev_down = {})
+                                 const moe::LaunchEvents& ev_gate_up = {}, const moe::LaunchEvents& ev_down = {},
+                                 const moe::SharedWeights& sh = {})
 {
     moe_status r;
-    if ((r = enqueue_chunk_gate_up(s, M, act_q, act_s, w13, s13, c, st, ev_gate_up)) != MOE_OK) return r;
-    if ((r = enqueue_requant(s, M, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), st)) != MOE_OK)
+    if ((r = enqueue_chunk_gate_up(s, M, act_q, act_s, w13, s13, c, st, ev_gate_up, sh)) != MOE_OK) return r;
+    if ((r = enqueue_requant(s, pair_rows(s, M, sh), c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2),
+                             c.at<float>(c.L.s2), st)) != MOE_OK)
         return r;
-    if ((r = enqueue_chunk_down(s, M, c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), false, w2, sw2, c, st,
-                                ev_down)) != MOE_OK)
+    if ((r = enqueue_chunk_down(s, M, c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), false, w2, sw2, c, st, ev_down,
+                                sh)) != MOE_OK)
         return r;
-    return enqueue_combine(s, M, topk_w, out, c, st);
+    return enqueue_combine(s, M, topk_w, out, c, st, has_shared(sh));
+}
+
+// A shared expert's four tensors: all given, 16-byte aligned codes.
+moe_status check_shared(const moe_shared_expert* sh)
+{
+    if (sh == nullptr) return MOE_OK;
+    if (sh->w13 == nullptr || sh->w13_scale == nullptr || sh->w2 == nullptr || sh->w2_scale == nullptr)
+        return fail(MOE_ERR_INVALID_ARG, "shared expert: w13, w13_scale, w2 and w2_scale must all be given");
+    if (!aligned16(sh->w13) || !aligned16(sh->w2))
+        return fail(MOE_ERR_ALIGNMENT, "shared expert: w13 and w2 must be 16-byte aligned");
+    return MOE_OK;
 }
 
 moe_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st)
@@ -251,9 +290,83 @@ moe_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st)
     return e == hipSuccess ? MOE_OK : hip_fail(e, "tap copy");
 }
 
+moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,
+                          const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                          const moe_shared_expert* shared, float* out, void* ws, size_t ws_bytes, void* stream,
+                          void* const* events)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(hidden); CHECK_PTR(router_w); CHECK_PTR(w13); CHECK_PTR(w13_scale);
+    CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(hidden); CHECK_ALIGN(router_w); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    if ((st = check_shared(shared)) != MOE_OK) return st;
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto ev = [&](int k) -> moe::LaunchEvents {
+        if (events == nullptr) return {};
+        return {static_cast<hipEvent_t>(events[2 * k]), static_cast<hipEvent_t>(events[2 * k + 1])};
+    };
+    const moe::SharedWeights sh = shared_weights(shared);
+    const Carved c = carve(shape, M, ws);
+    int32_t* ids = c.at<int32_t>(c.L.ids);
+    float* w = c.at<float>(c.L.w);
+    uint8_t* q = c.at<uint8_t>(c.L.act_q);
+    float* sc = c.at<float>(c.L.act_s);
+    float* h = c.at<float>(c.L.h);
+    if (chunked(M)) {
+        if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s, ev(0))) != MOE_OK) return st;
+        if ((st = enqueue_quant(shape, M, hidden, q, sc, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_topk(shape, M, ids, w, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_sort(shape, M, ids, c, s, has_shared(sh))) != MOE_OK) return st;
+        return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2), sh);
+    }
+    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, c, s, ev(1), sh)) != MOE_OK)
+        return st;
+    return enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s, ev(2), sh);
+}
+
+moe_status experts_forward(const moe_shape* shape, int32_t M, const uint8_t* act_fp8, const float* act_scale,
+                           const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                           const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                           const moe_shared_expert* shared, float* out, const moe_expert_taps* taps, void* ws,
+                           size_t ws_bytes, void* stream)
+{
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(act_fp8); CHECK_PTR(act_scale); CHECK_PTR(topk_ids); CHECK_PTR(topk_w);
+    CHECK_PTR(w13); CHECK_PTR(w13_scale); CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(act_fp8); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    if ((st = check_shared(shared)) != MOE_OK) return st;
+    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const moe::SharedWeights sh = shared_weights(shared);
+    const Carved c = carve(shape, M, ws);
+    if (chunked(M)) {
+        if ((st = enqueue_sort(shape, M, topk_ids, c, s, has_shared(sh))) != MOE_OK) return st;
+        if ((st = enqueue_chunk_experts(shape, M, act_fp8, act_scale, topk_w, w13, w13_scale, w2, w2_scale, out, c,
+                                        s, {}, {}, sh)) != MOE_OK)
+            return st;
+        if (taps == nullptr) return MOE_OK;
+        const int I = shape->inter, R = pair_rows(shape, M, sh);
+        if ((st = gather_out(taps->h, c.at<void>(c.L.h), R, I * 4, c, s)) != MOE_OK) return st;
+        if ((st = gather_out(taps->inter_fp8, c.at<void>(c.L.q2), R, I, c, s)) != MOE_OK) return st;
+        return gather_out(taps->inter_scale, c.at<void>(c.L.s2), R, 4, c, s);
+    }
+    float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
+    uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
+    float* s2_tap = taps ? taps->inter_scale : nullptr;
+    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, c, s, {},
+                              sh)) != MOE_OK)
+        return st;
+    return enqueue_down(shape, M, h, nullptr, nullptr, q2_tap, s2_tap, topk_w, w2, w2_scale, out, c, s, {}, sh);
+}
+
 }  // namespace
 
 extern "C" {
+
 
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens)
 {
@@ -276,33 +389,17 @@ moe_status moe_decode_forward_events(const moe_shape* shape, int32_t M, const ui
                                      const uint8_t* w2, const uint8_t* w2_scale, float* out, void* ws,
                                      size_t ws_bytes, void* stream, void* const* events)
 {
-    moe_status st = check_shape(shape, M);
-    if (st != MOE_OK) return st;
-    CHECK_PTR(hidden); CHECK_PTR(router_w); CHECK_PTR(w13); CHECK_PTR(w13_scale);
-    CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
-    CHECK_ALIGN(hidden); CHECK_ALIGN(router_w); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
-    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto ev = [&](int k) -> moe::LaunchEvents {
-        if (events == nullptr) return {};
-        return {static_cast<hipEvent_t>(events[2 * k]), static_cast<hipEvent_t>(events[2 * k + 1])};
-    };
-    const Carved c = carve(shape, M, ws);
-    int32_t* ids = c.at<int32_t>(c.L.ids);
-    float* w = c.at<float>(c.L.w);
-    uint8_t* q = c.at<uint8_t>(c.L.act_q);
-    float* sc = c.at<float>(c.L.act_s);
-    float* h = c.at<float>(c.L.h);
-    if (chunked(M)) {
-        if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s, ev(0))) != MOE_OK) return st;
-        if ((st = enqueue_quant(shape, M, hidden, q, sc, s)) != MOE_OK) return st;
-        if ((st = enqueue_chunk_topk(shape, M, ids, w, c, s)) != MOE_OK) return st;
-        if ((st = enqueue_sort(shape, M, ids, c, s)) != MOE_OK) return st;
-        return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2));
-    }
-    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, c, s, ev(1))) != MOE_OK) return st;
-    return enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s, ev(2));
+    return decode_forward(shape, M, hidden, router_w, w13, w13_scale, w2, w2_scale, nullptr, out, ws, ws_bytes,
+                          stream, events);
+}
+
+moe_status moe_decode_forward_shared(const moe_shape* shape, int32_t M, const uint16_t* hidden,
+                                     const uint16_t* router_w, const uint8_t* w13, const uint8_t* w13_scale,
+                                     const uint8_t* w2, const uint8_t* w2_scale, const moe_shared_expert* shared,
+                                     float* out, void* ws, size_t ws_bytes, void* stream, void* const* events)
+{
+    return decode_forward(shape, M, hidden, router_w, w13, w13_scale, w2, w2_scale, shared, out, ws, ws_bytes,
+                          stream, events);
 }
 
 moe_status moe_decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,
@@ -362,32 +459,18 @@ moe_status moe_experts_forward(const moe_shape* shape, int32_t M, const uint8_t*
                                const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
                                const moe_expert_taps* taps, void* ws, size_t ws_bytes, void* stream)
 {
-    moe_status st = check_shape(shape, M);
-    if (st != MOE_OK) return st;
-    CHECK_PTR(act_fp8); CHECK_PTR(act_scale); CHECK_PTR(topk_ids); CHECK_PTR(topk_w);
-    CHECK_PTR(w13); CHECK_PTR(w13_scale); CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
-    CHECK_ALIGN(act_fp8); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
-    if ((st = check_ws(shape, M, ws, ws_bytes)) != MOE_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const Carved c = carve(shape, M, ws);
-    if (chunked(M)) {
-        if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
-        if ((st = enqueue_chunk_experts(shape, M, act_fp8, act_scale, topk_w, w13, w13_scale, w2, w2_scale, out, c,
-                                        s)) != MOE_OK)
-            return st;
-        if (taps == nullptr) return MOE_OK;
-        const int I = shape->inter, K = shape->topk;
-        if ((st = gather_out(taps->h, c.at<void>(c.L.h), M, K, I * 4, c, s)) != MOE_OK) return st;
-        if ((st = gather_out(taps->inter_fp8, c.at<void>(c.L.q2), M, K, I, c, s)) != MOE_OK) return st;
-        return gather_out(taps->inter_scale, c.at<void>(c.L.s2), M, K, 4, c, s);
-    }
-    float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
-    uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
-    float* s2_tap = taps ? taps->inter_scale : nullptr;
-    if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, c, s)) !=
-        MOE_OK)
-        return st;
-    return enqueue_down(shape, M, h, nullptr, nullptr, q2_tap, s2_tap, topk_w, w2, w2_scale, out, c, s);
+    return experts_forward(shape, M, act_fp8, act_scale, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, nullptr, out,
+                           taps, ws, ws_bytes, stream);
+}
+
+moe_status moe_experts_forward_shared(const moe_shape* shape, int32_t M, const uint8_t* act_fp8,
+                                      const float* act_scale, const int32_t* topk_ids, const float* topk_w,
+                                      const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2,
+                                      const uint8_t* w2_scale, const moe_shared_expert* shared, float* out,
+                                      const moe_expert_taps* taps, void* ws, size_t ws_bytes, void* stream)
+{
+    return experts_forward(shape, M, act_fp8, act_scale, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, shared, out,
+                           taps, ws, ws_bytes, stream);
 }
 
 moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8, const float* act_scale,
@@ -405,18 +488,18 @@ moe_status moe_gate_up(const moe_shape* shape, int32_t M, const uint8_t* act_fp8
     if (chunked(M)) {
         if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
         if ((st = enqueue_chunk_gate_up(shape, M, act_fp8, act_scale, w13, w13_scale, c, s)) != MOE_OK) return st;
-        if ((st = enqueue_requant(shape, M, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), s)) !=
+        const int I = shape->inter, P = M * shape->topk;
+        if ((st = enqueue_requant(shape, P, c.at<float>(c.L.h), c.at<uint8_t>(c.L.q2), c.at<float>(c.L.s2), s)) !=
             MOE_OK)
             return st;
-        const int I = shape->inter, K = shape->topk;
-        if ((st = gather_out(h, c.at<void>(c.L.h), M, K, I * 4, c, s)) != MOE_OK) return st;
-        if ((st = gather_out(inter_fp8, c.at<void>(c.L.q2), M, K, I, c, s)) != MOE_OK) return st;
-        return gather_out(inter_scale, c.at<void>(c.L.s2), M, K, 4, c, s);
+        if ((st = gather_out(h, c.at<void>(c.L.h), P, I * 4, c, s)) != MOE_OK) return st;
+        if ((st = gather_out(inter_fp8, c.at<void>(c.L.q2), P, I, c, s)) != MOE_OK) return st;
+        return gather_out(inter_scale, c.at<void>(c.L.s2), P, 4, c, s);
     }
     if ((st = enqueue_gate_up(shape, M, topk_ids, nullptr, nullptr, act_fp8, act_scale, w13, w13_scale, h, c, s)) !=
         MOE_OK)
         return st;
-    return enqueue_requant(shape, M, h, inter_fp8, inter_scale, s);
+    return enqueue_requant(shape, M * shape->topk, h, inter_fp8, inter_scale, s);
 }
 
 moe_status moe_down_combine(const moe_shape* shape, int32_t M, const uint8_t* inter_fp8, const float* inter_scale,

@@ -220,21 +220,29 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
         atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    // expert offsets and slots (one thread per expert)
-    const int c = (tid < E) ? cnt[tid] : 0;
+    // expert offsets and slots (one thread per expert; thread E stands for the
+    // shared expert, whose M rows follow the routed pairs in one more slot)
+    const bool virt = a.shared != 0 && tid == E;
+    const int c = (tid < E) ? cnt[tid] : (virt ? a.M : 0);
     int total_pairs = 0, n_act = 0;
     const int off_e = block_excl_scan(c, tmp, total_pairs);
     const int slot_e = block_excl_scan(c > 0 ? 1 : 0, tmp, n_act);
-    if (tid < E) {
-        pre[tid] = off_e;
-        if (c > 0) {
-            a.cp.act_experts[slot_e] = tid;
-            a.cp.offsets[slot_e] = off_e;
-        }
+    const int rec_e = virt ? kSharedExpert : tid;
+    if (tid < E) pre[tid] = off_e;
+    if (c > 0) {
+        a.cp.act_experts[slot_e] = rec_e;
+        a.cp.offsets[slot_e] = off_e;
     }
     if (tid == 0) {
         *a.cp.n_act = n_act;
-        a.cp.offsets[n_act] = P;
+        a.cp.offsets[n_act] = total_pairs;
+    }
+    if (a.shared != 0) {
+        for (int t = tid; t < a.M; t += kSortThreads) {
+            a.cp.pair_token[P + t] = t;
+            a.cp.pair_src[P + t] = P + t;
+            a.pos_of[P + t] = P + t;
+        }
     }
     __syncthreads();
     if (dup == 0) {
@@ -291,11 +299,11 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
     if (c > 0) {
         for (int k = 0; k < full; ++k) {
             const int rows = c - k * kChunkRows;
-            a.chunks.rec[at4 + k] = make_int4(tid, off_e + k * kChunkRows, rows < kChunkRows ? rows : kChunkRows, 0);
+            a.chunks.rec[at4 + k] = make_int4(rec_e, off_e + k * kChunkRows, rows < kChunkRows ? rows : kChunkRows, 0);
         }
         if (last_tiles > 0) {
             const int idx = n4 + (last_tiles == 3 ? at3 : last_tiles == 2 ? n3 + at2 : n3 + n2 + at1);
-            a.chunks.rec[idx] = make_int4(tid, off_e + full * kChunkRows, rem, 0);
+            a.chunks.rec[idx] = make_int4(rec_e, off_e + full * kChunkRows, rem, 0);
         }
     }
     const int n_chunks = n4 + n3 + n2 + n1;
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const bool has_k = w < G::KSPLIT;
     const int ks0 = (has_k ? w : 0) * KQ;
     const int j0 = jq * kGuRows;
-    const uint8_t* w13e = a.w13 + (size_t)e * 2 * I * (H / 2);
+    const uint8_t* w13e = e == kSharedExpert ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
     i32x8 bg[NJ][KQ], bu[NJ][KQ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         const int row = tt * 16 + r;
         tok[tt] = a.cp.pair_token[off + (row < n ? row : n - 1)];
     }
-    const uint8_t* s13e = a.s13 + (size_t)e * 2 * I * SROW;
+    const uint8_t* s13e = e == kSharedExpert ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * SROW;
     copy_to_lds(sc_lds[0], s13e + (size_t)j0 * SROW, kGuRows * SROW);
     copy_to_lds(sc_lds[1], s13e + (size_t)(I + j0) * SROW, kGuRows * SROW);
     u32x4 alo[KQ], ahi[KQ];
@@ -479,10 +487,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     if (n == 0) return;                                 // whole workgroup: past the last chunk
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int n0 = nq * kDnRows;
+    const uint8_t* w2e = e == kSharedExpert ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
+    const uint8_t* sw2e = e == kSharedExpert ? a.sh.s2 : a.sw2 + (size_t)e * H * SROW;
     i32x8 b[NJ][KS];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
-        const uint8_t* wrow = a.w2 + ((size_t)e * H + n0 + (w * NJ + nj) * 16 + r) * (I / 2);
+        const uint8_t* wrow = w2e + (size_t)(n0 + (w * NJ + nj) * 16 + r) * (I / 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int kb = ks * 128 + 32 * g;             // first K of this lane's block
@@ -496,9 +506,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
     }
     if constexpr (SBYTES % 16 == 0) {
-        copy_to_lds(sc_lds, a.sw2 + ((size_t)e * H + n0) * SROW, SBYTES);
+        copy_to_lds(sc_lds, sw2e + (size_t)n0 * SROW, SBYTES);
     } else {
-        for (int i = threadIdx.x; i < SBYTES; i += 256) sc_lds[i] = a.sw2[((size_t)e * H + n0) * SROW + i];
+        for (int i = threadIdx.x; i < SBYTES; i += 256) sc_lds[i] = sw2e[(size_t)n0 * SROW + i];
     }
     u32x4 alo[KS], ahi[KS];
     float es[4];                                          // s2 of the rows this lane stores
@@ -569,7 +579,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 
 // ---------------------------------------------------------------------------
 // Combine: out[t, :] = sum_{j < K} w[t, j] * y[pos_of[t K + j], :], added in
-// j order.
+// j order, then (with a shared expert) + y[pos_of[M K + t], :].
 // ---------------------------------------------------------------------------
 template <int H>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
@@ -584,6 +594,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
             const float wj = a.w[t * a.K + j];
             const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)pos * H + c);
             s.x += wj * v.x; s.y += wj * v.y; s.z += wj * v.z; s.w += wj * v.w;
+        }
+        if (a.shared != 0) {
+            const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)a.pos_of[a.M * a.K + t] * H + c);
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
         *reinterpret_cast<float4*>(a.out + (size_t)t * H + c) = s;
     }

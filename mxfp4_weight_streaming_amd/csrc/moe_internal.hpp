@@ -14,10 +14,22 @@ constexpr int kMaxGemvTokens = 8;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxPairs = kMaxGemvTokens * kMaxTopK;
+// With a shared expert every token adds one pair (row P + t of the
+// intermediates) in one more slot, whose expert id is kSharedExpert.
+constexpr int kMaxPairsExt = kMaxPairs + kMaxGemvTokens;
+constexpr int kSharedExpert = -1;
 // Largest token count of the chunk path (M > kMaxGemvTokens): its M*K pairs
 // are sorted by expert in one workgroup's LDS.
 constexpr int kMaxChunkTokens = 2048;
 constexpr int kMaxChunkPairs = kMaxChunkTokens * kMaxTopK;
+
+// The shared expert's weights (one expert of the routed layout), or all null.
+struct SharedWeights {
+    const uint8_t* w13;    // [2I,H/2]
+    const uint8_t* s13;    // [2I,H/32]
+    const uint8_t* w2;     // [H,I/2]
+    const uint8_t* s2;     // [H,I/32]
+};
 
 // Token -> expert compaction as published in the workspace.
 struct Compaction {
@@ -43,6 +55,7 @@ struct RouteSrc {
     int M, E, K;
     const float* logits;   // [M,E] or nullptr
     const int32_t* ids;    // [M,K] used when logits is nullptr
+    int shared;            // 1: append the shared expert's slot
 };
 
 struct TopkArgs {
@@ -61,7 +74,8 @@ struct GateUpArgs {
     const uint8_t* s13;    // [E,2I,H/32]
     const uint8_t* act_q;  // [M,H]
     const float* act_s;    // [M]
-    float* h;              // [M*K,I]
+    float* h;              // [M*K (+M),I]
+    SharedWeights sh;      // read when the compaction holds the shared slot
 };
 
 struct DownArgs {
@@ -76,6 +90,7 @@ struct DownArgs {
     const float* topk_w;   // [M*K]
     Compaction cp;         // read
     float* out;            // [M,H]
+    SharedWeights sh;      // non-null w2: the compaction's last slot is the shared expert (weight 1)
 };
 
 struct RequantArgs {
@@ -118,8 +133,9 @@ struct SortArgs {
     const int32_t* ids;    // [M,K]; out-of-range ids are clamped into [0, E)
     int M, K, E;
     Compaction cp;         // written
-    int32_t* pos_of;       // [M*K]
+    int32_t* pos_of;       // [M*K (+M)]
     ChunkList chunks;      // written
+    int shared;            // 1: the shared expert's M rows follow as one more slot
 };
 
 struct ChunkGateUpArgs {
@@ -129,7 +145,8 @@ struct ChunkGateUpArgs {
     const uint8_t* s13;    // [E,2I,H/32]
     const uint8_t* act_q;  // [M,H]
     const float* act_s;    // [M]
-    float* h;              // [M*K,I] in sorted order
+    float* h;              // [M*K (+M),I] in sorted order
+    SharedWeights sh;
 };
 
 struct ChunkDownArgs {
@@ -140,7 +157,8 @@ struct ChunkDownArgs {
     const uint8_t* q2;     // [M*K,I] E4M3 intermediate
     const float* s2;       // [M*K]
     int by_pair;           // 0: q2/s2 rows in sorted order; 1: in pair order
-    float* y;              // [M*K,H] expert outputs (s2 applied) in sorted order
+    float* y;              // [M*K (+M),H] expert outputs (s2 applied) in sorted order
+    SharedWeights sh;
 };
 
 struct CombineArgs {
@@ -149,6 +167,7 @@ struct CombineArgs {
     const float* w;        // [M*K] router weights in pair order
     int M, K;
     float* out;            // [M,H]
+    int shared;            // 1: add the shared expert's row y[pos_of[M*K + t]] (weight 1)
 };
 
 // Workspace carving.  No state is carried between calls: every call writes
@@ -162,9 +181,11 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline WsLayout ws_layout(int H, int I, int E, int K, int M)
 {
+    // room for a shared expert is always kept: one more slot and M more pairs
     WsLayout L{};
     const size_t P = (size_t)M * K;
-    const size_t S = (size_t)(E < (int)P ? E : (int)P);
+    const size_t Pe = P + (size_t)M;
+    const size_t S = (size_t)(E < (int)P ? E : (int)P) + 1;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     L.logits = take((size_t)M * E * 4);
@@ -175,15 +196,15 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     L.n_act = take(4);
     L.act_experts = take(S * 4);
     L.offsets = take((S + 1) * 4);
-    L.pair_token = take(P * 4);
-    L.pair_src = take(P * 4);
-    L.h = take(P * I * 4);
-    L.q2 = take(P * I);
-    L.s2 = take(P * 4);
+    L.pair_token = take(Pe * 4);
+    L.pair_src = take(Pe * 4);
+    L.h = take(Pe * I * 4);
+    L.q2 = take(Pe * I);
+    L.s2 = take(Pe * 4);
     const bool chunk = M > kMaxGemvTokens;
-    L.pos_of = take(chunk ? P * 4 : 0);
-    L.y = take(chunk ? P * (size_t)H * 4 : 0);
-    const size_t C = chunk ? (size_t)chunk_bound((int)S, (int)P) : 0;
+    L.pos_of = take(chunk ? Pe * 4 : 0);
+    L.y = take(chunk ? Pe * (size_t)H * 4 : 0);
+    const size_t C = chunk ? (size_t)chunk_bound((int)S, (int)Pe) : 0;
     L.n_chunks = take(chunk ? 4 : 0);
     L.chunk_rec = take(C * 16);
     L.total = off;

@@ -76,10 +76,10 @@ struct alignas(16) RouteLds {
     int32_t ids[kMaxPairs];
     float w[kMaxPairs];
     int32_t n_act;
-    int32_t act_experts[kMaxPairs];
-    int32_t offsets[kMaxPairs + 1];
-    int32_t pair_token[kMaxPairs];
-    int32_t pair_src[kMaxPairs];
+    int32_t act_experts[kMaxPairs + 1];
+    int32_t offsets[kMaxPairs + 2];
+    int32_t pair_token[kMaxPairsExt];
+    int32_t pair_src[kMaxPairsExt];
 };
 
 // One wave; lane p < P owns pair p with expert e_p.  Its compacted position
@@ -178,6 +178,21 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
         } else {
             compact_wave(P, K, r);
         }
+        if (src.shared) {
+            // the shared expert's slot follows the routed ones: every token,
+            // pair row P + t (its weight, 1, is applied by the down kernel)
+            const int lane = tid & 63;
+            if (lane < M) {
+                r.pair_token[P + lane] = lane;
+                r.pair_src[P + lane] = P + lane;
+            }
+            if (lane == 0) {
+                const int n = r.n_act;
+                r.act_experts[n] = kSharedExpert;
+                r.offsets[n + 1] = P + M;
+                r.n_act = n + 1;
+            }
+        }
     }
     __syncthreads();
 }
@@ -186,10 +201,12 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
 __device__ void publish_route(const RouteLds& r, const RouteSrc& src, int32_t* ids_out, float* w_out,
                               const Compaction& cp)
 {
-    const int tid = threadIdx.x, P = src.M * src.K;
+    const int tid = threadIdx.x, P = src.M * src.K, Pe = P + (src.shared ? src.M : 0);
     if (tid < P) {
         if (ids_out != nullptr) ids_out[tid] = r.ids[tid];
         if (w_out != nullptr && src.logits != nullptr) w_out[tid] = r.w[tid];
+    }
+    if (tid < Pe) {
         cp.pair_token[tid] = r.pair_token[tid];
         cp.pair_src[tid] = r.pair_src[tid];
     }
@@ -348,10 +365,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     auto issue = [&](int item, Stage& st) {
         const int slot = item / BPE, rb = item % BPE;
         const int e = rl.act_experts[slot];
+        const bool shared = e == kSharedExpert;
         const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
-        const u32x4* grow = (const u32x4*)(a.w13 + ((size_t)e * 2 * I + r) * (H / 2));
+        const uint8_t* w13e = shared ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
+        const uint8_t* s13e = shared ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * CH;
+        const u32x4* grow = (const u32x4*)(w13e + (size_t)r * (H / 2));
         const u32x4* urow = grow + (size_t)I * CH;
-        const uint8_t* gsc = a.s13 + ((size_t)e * 2 * I + r) * CH;
+        const uint8_t* gsc = s13e + (size_t)r * CH;
         const uint8_t* usc = gsc + (size_t)I * CH;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -525,18 +545,21 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, RPB = G::kRowsPerBlock;
     extern __shared__ u32x4 q2h[];                 // [pair][q][chunk] of 8 halves
     __shared__ float red[G::kWaves][RPB][MT];
-    __shared__ float s2l[kMaxPairs];
+    __shared__ float s2l[kMaxPairsExt];
 
-    const int P = a.M * a.K;
-    const int n_act = min(*a.cp.n_act, min(a.E, P));
+    const bool shared = a.sh.w2 != nullptr;
+    const int P = a.M * a.K, Pe = P + (shared ? a.M : 0);   // routed pairs, plus the shared expert's rows
+    const int n_act = min(*a.cp.n_act, min(a.E, P) + (shared ? 1 : 0));
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane % LPR, grp = lane / LPR;
     const int n = blockIdx.x * RPB + grp;
 
     auto load_slot = [&](int slot, u32x4* wv, uint32_t* sv) {
-        const int e = min(max(a.cp.act_experts[slot], 0), a.E - 1);
-        const u32x4* row = (const u32x4*)(a.w2 + ((size_t)e * H + n) * (I / 2));
-        const uint8_t* sc = a.sw2 + ((size_t)e * H + n) * CH;
+        const int ea = a.cp.act_experts[slot];
+        const bool sh = shared && ea == kSharedExpert;
+        const int e = min(max(ea, 0), a.E - 1);
+        const u32x4* row = (const u32x4*)((sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2)) + (size_t)n * (I / 2));
+        const uint8_t* sc = (sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH) + (size_t)n * CH;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) wv[i] = load_stream(row + li + LPR * i);
 #pragma unroll
@@ -552,7 +575,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     R rows[RB];
     if constexpr (FROM_H) {
 #pragma unroll
-        for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(wave + G::kWaves * j, P - 1));
+        for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(wave + G::kWaves * j, Pe - 1));
     }
     int slot = wave;
     u32x4 wv[CPL];
@@ -562,15 +585,15 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     if constexpr (FROM_H) {
         _Float16* q16 = reinterpret_cast<_Float16*>(q2h);
         const bool tap = blockIdx.x == 0 && a.q2_out != nullptr;
-        for (int base = 0; base < P; base += G::kWaves * RB) {
+        for (int base = 0; base < Pe; base += G::kWaves * RB) {
             if (base > 0) {
 #pragma unroll
-                for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(base + wave + G::kWaves * j, P - 1));
+                for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(base + wave + G::kWaves * j, Pe - 1));
             }
 #pragma unroll
             for (int j = 0; j < RB; ++j) {
                 const int p = base + wave + G::kWaves * j;
-                if (p >= P) break;
+                if (p >= Pe) break;
                 const float sc = rows[j].scale();
                 uint32_t codes[R::NCODE];
                 rows[j].encode(sc, codes);
@@ -633,9 +656,9 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
             e2m1x8_to_half(wv[i].z, hw + 16 * i + 8);
             e2m1x8_to_half(wv[i].w, hw + 16 * i + 12);
         }
-        const int q0 = min(max(a.cp.offsets[slot], 0), P), q1 = min(a.cp.offsets[slot + 1], P);
+        const int q0 = min(max(a.cp.offsets[slot], 0), Pe), q1 = min(a.cp.offsets[slot + 1], Pe);
         for (int qq = q0; qq < q1; ++qq) {
-            const int p = min(max(a.cp.pair_src[qq], 0), P - 1);
+            const int p = min(max(a.cp.pair_src[qq], 0), Pe - 1);
             const int tok = a.cp.pair_token[qq];
             float d = 0.0f;
 #pragma unroll
@@ -646,7 +669,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
                 d += ldexp_e8m0(block_dot(hw + 16 * i, a0, a1, a2, a3), sv[i]);
             }
             d = group_sum<LPR>(d);
-            const float coef = a.topk_w[p] * s2l[p];
+            const float coef = (p < P ? a.topk_w[p] : 1.0f) * s2l[p];
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 if (t == tok) acc[t] = fmaf(coef, d, acc[t]);
@@ -721,7 +744,9 @@ template <int H, int I, int MT>
 static hipError_t launch_down_t(const DownArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
     using G = DownGeom<H, I>;
-    const size_t lds = (size_t)a.M * a.K * I * 2;
+    // the shared expert's rows come only from h (the caller-given q2 path is routed-only)
+    if (a.sh.w2 != nullptr && a.h == nullptr) return hipErrorInvalidValue;
+    const size_t lds = (size_t)(a.M * a.K + (a.sh.w2 != nullptr ? a.M : 0)) * I * 2;
     const void* fn = a.h != nullptr ? (const void*)down_kernel<H, I, MT, true> : (const void*)down_kernel<H, I, MT, false>;
     if (lds > 64 * 1024) {   // above the default dynamic-LDS limit (gfx950 has 160 KiB per CU)
         hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -95,6 +95,14 @@ def expert_weights(seed: int, H: int, I: int, E: int) -> Weights:
     return Weights(H, I, E, wr, w13, s13, w2, s2)
 
 
+def shared_expert(seed: int, H: int, I: int):
+    """One shared expert drawn like a routed one: (w13 [2I,H/2], s13 [2I,H/32],
+    w2 [H,I/2], s2 [H,I/32])."""
+    rng = np.random.default_rng(seed)
+    return (mxfp4_codes(rng, 1, 2 * I, H)[0], e8m0_scales(rng, 1, 2 * I, H)[0],
+            mxfp4_codes(rng, 1, H, I)[0], e8m0_scales(rng, 1, H, I)[0])
+
+
 def with_router(w: Weights, wr: np.ndarray) -> Weights:
     return Weights(w.H, w.I, w.E, np.ascontiguousarray(wr, np.uint16), w.w13, w.s13, w.w2, w.s2)
 

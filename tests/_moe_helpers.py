@@ -72,18 +72,3 @@ def fp8_code_mismatches_ok(gpu_q: np.ndarray, ref_q: np.ndarray, ref_y: np.ndarr
         if not (same_sign and adjacent and near):
             bad.append(i)
     return len(idx[0]), bad
-
-
-def fp8_code_mismatches_adjacent(gpu_q: np.ndarray, ref_q: np.ndarray):
-    """Every differing code must be an adjacent code of the same sign (one
-    rounding step apart).  Returns (n_mismatch, list of offending indices)."""
-    vals = e4m3_values()
-    bad = []
-    idx = np.nonzero(gpu_q != ref_q)
-    for i in zip(*idx):
-        g, r = int(gpu_q[i]), int(ref_q[i])
-        if vals[g] == vals[r]:
-            continue
-        if not ((g & 0x80) == (r & 0x80) and abs((g & 0x7F) - (r & 0x7F)) == 1):
-            bad.append(i)
-    return len(idx[0]), bad

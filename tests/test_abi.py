@@ -113,3 +113,27 @@ def test_lm_head_validation(moe):
     assert L.moe_lm_head_forward(a, 9, a, a, 16, 2560, a, None) == -2     # above 8 tokens
     assert L.moe_lm_head_forward(a, 0, a, a, 16, 2560, a, None) == -1
     assert L.moe_lm_head_forward(a, 1, a, None, 16, 2560, a, None) == -1
+
+
+def test_shared_expert_validation(moe):
+    s = _shape(moe)
+    L = moe.raw()
+    a = 1 << 20
+    ws_need = moe.moe_workspace_bytes(s, 4)
+    # the workspace of moe_workspace_bytes already covers the shared expert's rows
+    assert ws_need >= (4 * 8 + 4) * 768 * 4
+    bad = moe.MoeSharedExpert(a, None, a, a)
+    assert L.moe_decode_forward_shared(ctypes.byref(s), 4, a, a, a, a, a, a, ctypes.byref(bad), a, a, ws_need,
+                                       None, None) == -1
+    assert "shared" in moe.moe_last_error()
+    mis = moe.MoeSharedExpert(a + 4, a, a, a)
+    assert L.moe_decode_forward_shared(ctypes.byref(s), 4, a, a, a, a, a, a, ctypes.byref(mis), a, a, ws_need,
+                                       None, None) == -3
+    mis2 = moe.MoeSharedExpert(a, a, a + 8, a)
+    assert L.moe_experts_forward_shared(ctypes.byref(s), 1, a, a, a, a, a, a, a, a, ctypes.byref(mis2), a, None, a,
+                                        ws_need, None) == -3
+    ok = moe.MoeSharedExpert(a, a, a, a)
+    assert L.moe_experts_forward_shared(ctypes.byref(s), 1, a, a, a, a, a, a, a, a, ctypes.byref(ok), a, None, a,
+                                        16, None) == -4
+    assert L.moe_decode_forward_shared(ctypes.byref(s), 0, a, a, a, a, a, a, ctypes.byref(ok), a, a, ws_need,
+                                       None, None) == -1
