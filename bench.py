@@ -20,6 +20,11 @@ Reported (one JSON line on stdout):
                its algorithmic bytes (the selected experts' gate/up codes and
                scales) over its execution time, from start/stop HIP events its
                launch stamps (plain launches on the bench stream)
+  by_tokens    the same per token count of --tokens (1..8)
+  shared_expert  the walk again with the model's shared expert in every layer
+  chunk        the 512-token chunk layer (grouped scaled FP4xFP8 MFMA) and its
+               matrix-core rate against the FP4 and FP8 dense peaks
+  lm_head      the FP8 LM-head GEMV (vocabulary 157,184) per token count
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -68,6 +73,8 @@ def parse():
     p.add_argument("--chunk-steps", type=int, default=400, help="timed chunk layer forwards")
     p.add_argument("--lm-head-vocab", type=int, default=157184, help="vocabulary of the FP8 LM-head GEMV (0: skip)")
     p.add_argument("--lm-head-steps", type=int, default=400, help="timed LM-head GEMV calls per token count")
+    p.add_argument("--shared-steps", type=int, default=4000,
+                   help="layer forwards timed again with a shared expert per layer (0: skip)")
     return p.parse_args()
 
 
@@ -103,13 +110,17 @@ def main() -> int:
     log(f"path: {path}")
     log(f"drawing {L} layers of weights on the GPU ({L * (EXPERT_BYTES * E + ROUTER_BYTES) / 2**30:.1f} GiB)")
     stack = synth.device_stack(L, H, I, E, seed=1234)
+    shared_layers = synth.device_shared(L, H, I, seed=4321) if args.shared_steps > 0 else None
     stream = torch.cuda.Stream()
     ws = moe.workspace(shp, 8)
     out = torch.empty((8, H), dtype=torch.float32, device="cuda")
 
-    def fwd(l, x, M, events=None):
+    def fwd(l, x, M, events=None, shared=False):
         Ly = stack[l]
-        if events is None:
+        if shared:
+            moe.moe_decode_forward_shared(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"],
+                                          shared_layers[l], out, ws)
+        elif events is None:
             moe.moe_decode_forward(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws)
         else:
             moe.moe_decode_forward_events(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws,
@@ -117,6 +128,7 @@ def main() -> int:
 
     results = {}
     kernel_stats = {}
+    shared_results = {}
     token_counts = [int(v) for v in args.tokens.split(",")]
     for M in token_counts:
         xs = synth.device_hidden(L * reps, M, H, seed=10_000 + M)
@@ -213,6 +225,42 @@ def main() -> int:
                            "gate_up_gbs": gu_bytes / (kmean["gate_up"] * 1e-6) / 1e9}
         log(f"M={M}: kernel means (us) {kmean}, gate_up {kernel_stats[M]['gate_up_gbs']:.0f} GB/s")
 
+        if shared_layers is not None:
+            # the same walk with the model's shared expert in every layer
+            # (one more expert's weights per layer, same kernels)
+            with torch.cuda.stream(stream):
+                for r in range(reps):
+                    for l in range(L):
+                        fwd(l, xs[r * L + l], M, shared=True)
+                torch.cuda.synchronize()
+                gsh = []
+                for r in range(reps):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        for l in range(L):
+                            fwd(l, xs[r * L + l], M, shared=True)
+                    gsh.append(g)
+                for i in range(reps):
+                    gsh[i].replay()
+                torch.cuda.synchronize()
+                n_sh = max(1, math.ceil(args.shared_steps / L))
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                for i in range(n_sh):
+                    gsh[i % reps].replay()
+                s1.record(stream)
+                torch.cuda.synchronize()
+            sms = s0.elapsed_time(s1)
+            sbytes = sum(rep_bytes[i % reps] + L * EXPERT_BYTES for i in range(n_sh))
+            shared_results[M] = {"us_per_layer": round(sms * 1e3 / (n_sh * L), 3),
+                                 "gbs": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                                 "pct_of_hbm_peak": round(100 * sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                 "layers": n_sh * L}
+            log(f"M={M} with a shared expert: {shared_results[M]['us_per_layer']:.2f} us/layer, "
+                f"{shared_results[M]['gbs']:.0f} GB/s")
+            del gsh
+
         results[M] = {"us_per_layer": ms * 1e3 / steps, "gbs": gbs, "steps": steps, "ms": ms,
                       "mean_distinct_experts": float(n_act.mean()),
                       "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9}
@@ -274,6 +322,7 @@ def main() -> int:
                      "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
+        "shared_expert": {"by_tokens": {str(M): v for M, v in shared_results.items()}} if shared_results else None,
         "chunk": chunk,
         "lm_head": lm_head,
         "cpu_baseline": cpu,

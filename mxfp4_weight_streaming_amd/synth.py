@@ -186,6 +186,22 @@ def device_stack(n_layers: int, H: int, I: int, E: int, seed: int, device="cuda"
     return layers
 
 
+def device_shared(n_layers: int, H: int, I: int, seed: int, device="cuda"):
+    """n_layers shared experts on the device: tuples (w13, s13, w2, s2) drawn
+    like one routed expert each."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(n_layers):
+        w13 = torch.randint(0, 256, (2 * I, H // 2), generator=g, device=device, dtype=torch.uint8)
+        s13 = torch.randint(SCALE_LO, SCALE_HI + 1, (2 * I, H // 32), generator=g, device=device, dtype=torch.uint8)
+        w2 = torch.randint(0, 256, (H, I // 2), generator=g, device=device, dtype=torch.uint8)
+        s2 = torch.randint(SCALE_LO, SCALE_HI + 1, (H, I // 32), generator=g, device=device, dtype=torch.uint8)
+        out.append((w13, s13, w2, s2))
+    return out
+
+
 def device_hidden(n: int, M: int, H: int, seed: int, device="cuda"):
     """n independent [M, H] bf16 hidden batches (as uint16 bit views)."""
     import torch
