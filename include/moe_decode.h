@@ -58,11 +58,13 @@
  * every buffer alive until the stream has passed the call.  Inputs are only
  * read.  A workspace serves one call in flight at a time; calls with distinct
  * workspaces may run concurrently.  The library keeps no other global state
- * except a thread-local copy of the last error message.
+ * except a thread-local copy of the last error message and the registry of
+ * modules loaded by moe_jit_load.
  *
  * Errors.  Every argument is checked before anything is enqueued; on any
  * error nothing is enqueued and the status says why.  No C++ exception
- * crosses this interface.  A shape outside the compiled set is
+ * crosses this interface.  A shape with no kernels on the current device
+ * (neither compiled in nor loaded by moe_jit_load) is
  * MOE_ERR_UNSUPPORTED_SHAPE -- there is never a silent fallback to a slower
  * or different kernel (the pages warn that a silent fallback made a draft
  * model misread FP8 weights as BF16: [EN] "What are the 3 optimizations?",
@@ -90,7 +92,8 @@ typedef enum {
     MOE_ERR_UNSUPPORTED_SHAPE = -2, /* (H, I, E, K, M) outside the compiled set  */
     MOE_ERR_ALIGNMENT = -3,         /* a tensor base is not 16-byte aligned       */
     MOE_ERR_WORKSPACE = -4,         /* workspace missing, misaligned or too small */
-    MOE_ERR_HIP = -5                /* a HIP launch or copy failed                */
+    MOE_ERR_HIP = -5,               /* a HIP launch or copy failed                */
+    MOE_ERR_JIT = -6                /* run-time compilation or its cache failed   */
 } moe_status;
 
 /* H = hidden, I = expert intermediate, E = routed experts, K = experts per token. */
@@ -278,6 +281,60 @@ const char* moe_status_string(moe_status status);
 
 /* The last error message recorded on this thread ("" if none). */
 const char* moe_last_error(void);
+
+/* ---- Run-time compilation for other layer shapes --------------------------
+ *
+ * The kernels above are compiled into this library for (H, I) = (256, 64) and
+ * (2560, 768), and the LM-head GEMV for hidden 512 and 2560.  Other shapes get
+ * the same kernels compiled at run time with hipRTC for their (H, I) and the
+ * GPU, the way the pages' MoE backend compiles per shape and caches the
+ * binaries ([EN] "What are the 3 optimizations?", item 1; [ZH]
+ * "三项优化分别做了什么").  One module per (H, I) holds the decode-path kernels
+ * (M <= 8), the chunk-path kernels where their blocking fits (H % 256 == 0,
+ * I % 32 == 0) and the LM-head GEMV for hidden H where it fits (H % 256 == 0,
+ * H <= 4096).  Compiled code objects are kept in a cache directory (cache_dir;
+ * NULL or "" means $MOE_JIT_CACHE_DIR, else $XDG_CACHE_HOME/moe_decode_jit, else
+ * $HOME/.cache/moe_decode_jit), one file per shape named by a 64-bit hash of
+ * the kernel sources, compile options, compiler version, target and shape;
+ * a file whose header, kernel list or checksum does not match is rebuilt.
+ * Files are written to a temporary name and renamed, so concurrent builders
+ * never see a partial file.
+ *
+ * Nothing is compiled implicitly: a call with a shape that has no kernels on
+ * the current device fails with MOE_ERR_UNSUPPORTED_SHAPE.  These calls
+ * allocate host memory and (load) device code; they are set-up calls, not for
+ * stream capture.  The library's module registry is process-wide and
+ * thread-safe. */
+typedef struct {
+    int32_t from_cache;      /* 1: the code object came from the cache file; 0: compiled by this call */
+    int32_t has_chunk_path;  /* the module holds the chunk-path kernels (M > 8)                    */
+    int32_t has_lm_head;     /* the module holds the LM-head GEMV for hidden H                    */
+    int32_t num_kernels;     /* kernels in the module                                              */
+    double  seconds;         /* wall time of the call                                              */
+    char    cache_file[1024];
+} moe_jit_report;
+
+/* Compile the kernels of shape->hidden, shape->inter for `arch` ("gfx950",
+ * optionally with ":feature" suffixes) into the cache, or find them there.
+ * Needs no GPU (a build farm can fill a cache for later use).  report may be
+ * NULL.  MOE_ERR_UNSUPPORTED_SHAPE for a shape without kernel geometry or
+ * another target; MOE_ERR_JIT with the compiler log for a failed compile or
+ * an unusable cache directory. */
+moe_status moe_jit_build(const moe_shape* shape, const char* arch, const char* cache_dir,
+                         moe_jit_report* report);
+
+/* moe_jit_build for the current device, then load the module on it; later
+ * calls on this device with this (H, I) run its kernels.  prefer != 0 makes
+ * them win over compiled-in kernels of the same shape (to check that the two
+ * agree); otherwise compiled-in kernels are used where they exist.  Loading a
+ * shape again replaces its earlier module on this device (no work using the
+ * old one may be pending).  MOE_ERR_HIP if the code object does not load. */
+moe_status moe_jit_load(const moe_shape* shape, const char* cache_dir, int32_t prefer,
+                        moe_jit_report* report);
+
+/* Unload the module of (H, I) from the current device; returns the number of
+ * modules removed (0 or 1).  No work using it may be pending. */
+int32_t moe_jit_unload(const moe_shape* shape);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ MOE_ERR_UNSUPPORTED_SHAPE = -2
 MOE_ERR_ALIGNMENT = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_JIT = -6
 
 
 class MoeShape(ctypes.Structure):
@@ -52,6 +53,16 @@ class MoeExpertTaps(ctypes.Structure):
 class MoeSharedExpert(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p)]
+
+
+class MoeJitReport(ctypes.Structure):
+    _fields_ = [("from_cache", ctypes.c_int32), ("has_chunk_path", ctypes.c_int32), ("has_lm_head", ctypes.c_int32),
+                ("num_kernels", ctypes.c_int32), ("seconds", ctypes.c_double), ("cache_file", ctypes.c_char * 1024)]
+
+    def as_dict(self) -> dict:
+        return {"from_cache": bool(self.from_cache), "has_chunk_path": bool(self.has_chunk_path),
+                "has_lm_head": bool(self.has_lm_head), "num_kernels": self.num_kernels, "seconds": self.seconds,
+                "cache_file": self.cache_file.decode()}
 
 
 _V = ctypes.c_void_p
@@ -80,6 +91,9 @@ _SIGNATURES = {
     "moe_lm_head_quantize": (ctypes.c_int, [_V, _i32, _i32, _V, _V, _V]),
     "moe_lm_head_forward": (ctypes.c_int, [_V, _i32, _V, _V, _i32, _i32, _V, _V]),
     "moe_path_info": (ctypes.c_int, [_S, _i32, ctypes.c_char_p, _sz]),
+    "moe_jit_build": (ctypes.c_int, [_S, ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(MoeJitReport)]),
+    "moe_jit_load": (ctypes.c_int, [_S, ctypes.c_char_p, _i32, ctypes.POINTER(MoeJitReport)]),
+    "moe_jit_unload": (_i32, [_S]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -271,6 +285,30 @@ def moe_lm_head_forward(x_bf16, q, scale, logits, stream=None):
     V = q.shape[0]
     _check(_lib.moe_lm_head_forward(_p(x_bf16), M, _p(q), _p(scale), V, H, _p(logits), _stream(stream)),
            "moe_lm_head_forward")
+
+
+def _path_arg(p):
+    return None if p is None else os.fsencode(p)
+
+
+def moe_jit_build(shp: MoeShape, arch: str = "gfx950", cache_dir=None) -> dict:
+    """Compile the kernels of (H, I) for `arch` into the cache (no GPU needed)."""
+    r = MoeJitReport()
+    _check(_lib.moe_jit_build(ctypes.byref(shp), arch.encode(), _path_arg(cache_dir), ctypes.byref(r)),
+           "moe_jit_build")
+    return r.as_dict()
+
+
+def moe_jit_load(shp: MoeShape, cache_dir=None, prefer: bool = False) -> dict:
+    """Compile or find (H, I) in the cache and load it on the current device."""
+    r = MoeJitReport()
+    _check(_lib.moe_jit_load(ctypes.byref(shp), _path_arg(cache_dir), 1 if prefer else 0, ctypes.byref(r)),
+           "moe_jit_load")
+    return r.as_dict()
+
+
+def moe_jit_unload(shp: MoeShape) -> int:
+    return _lib.moe_jit_unload(ctypes.byref(shp))
 
 
 def moe_path_info(shp: MoeShape, M: int) -> tuple[int, str]:

@@ -9,7 +9,9 @@
 //           integer round-to-nearest-even and saturation to 448.
 #pragma once
 
+#ifndef __HIPCC_RTC__
 #include <hip/hip_runtime.h>
+#endif
 #include <stdint.h>
 
 namespace moe {

@@ -1,0 +1,716 @@
+// gemv_kernels.hpp -- gfx950 kernels of the W4A8 MoE decode layer (M <= 8 tokens),
+// device code only: compiled ahead of time through moe_kernels.hip and at run
+// time by hipRTC for shapes outside the ahead-of-time set.
+//
+// The pages find batch-1 MoE decode bound by reading expert weights ([EN]
+// "Why is MoE decoding on DGX Spark memory-bound?"), so the kernels are built
+// around streaming MXFP4 bytes from HBM once, with wide loads issued before
+// any dependent work.  A layer is three kernels on one stream:
+//   router_kernel   fp32 router GEMV (one wave per expert row) and per-token
+//                   FP8 quantisation of the activations.
+//   gate_up_kernel  every workgroup derives the routing from the logits
+//                   (top-K, renormalised weights, token->expert compaction:
+//                   [EN] "What is Ling 3.0...", 8 routed experts per token;
+//                   [EN] "What are the 3 optimizations?", item 3: a 4-token
+//                   verify touches up to 32 experts), then streams the fused
+//                   gate/up MXFP4 GEMV of (expert, row block) items with the
+//                   SiLU(gate)*up epilogue ([EN] same section, item 1: the
+//                   768-wide expert layer).  (Pulling the down weights into
+//                   the memory-side cache here was measured slower: it adds
+//                   their bytes to this kernel's stream for little gain in
+//                   the next.)
+//   down_kernel     requantises the intermediate to FP8 per (token, expert)
+//                   row while its weight loads are in flight, then the down
+//                   GEMV over all selected experts and the router-weighted
+//                   combine in a fixed order (no float atomics).
+// Workgroups never synchronise with each other inside a kernel: on this chip
+// a device-scope release costs every workgroup a serialised L2 write-back,
+// far dearer than repeating a little work in every workgroup.
+// The M <= 8 path is a GEMV: it uses the vector ALU (dot2 on exactly decoded
+// f16 operands, fp32 accumulation), not the matrix cores.
+//   [EN] = "NVIDIA Shows 3 Ways to Speed Up MoE Inference on DGX Spark,
+//          Lifting Ling-3.0-flash Throughput 42.5%"
+#pragma once
+
+#include "device_common.hpp"
+#include "moe_types.hpp"
+#include "topk_wave.hpp"
+
+namespace moe {
+
+
+// ---------------------------------------------------------------------------
+// Per-token activation quantisation (one workgroup, one token).
+// s = amax / 448 (1 for an all-zero row), q = E4M3(x / s), both divisions
+// correctly rounded binary32 divisions.
+// ---------------------------------------------------------------------------
+template <int H>
+__device__ void quantize_token(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                               float* __restrict__ s_out, float* red)
+{
+    float m = 0.0f;
+    for (int k = threadIdx.x; k < H; k += blockDim.x) m = fmaxf(m, fabsf(bf16_bits_to_f32(x[k])));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float amax = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    for (int k = threadIdx.x; k < H; k += blockDim.x) q[k] = (uint8_t)e4m3_encode(bf16_bits_to_f32(x[k]) / s);
+    if (threadIdx.x == 0) *s_out = s;
+    __syncthreads();
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                                    float* __restrict__ s)
+{
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    quantize_token<H>(x + (size_t)t * H, q + (size_t)t * H, s + t, red);
+}
+
+// ---------------------------------------------------------------------------
+// Routing prologue, run by every thread of a workgroup: top-K (from logits) or
+// caller ids, then token->expert compaction, all in LDS.  Distinct experts get
+// slots in ascending id; the pairs of a slot are in ascending token order.
+// ---------------------------------------------------------------------------
+struct alignas(16) RouteLds {
+    int32_t ids[kMaxPairs];
+    float w[kMaxPairs];
+    int32_t n_act;
+    int32_t act_experts[kMaxPairs + 1];
+    int32_t offsets[kMaxPairs + 2];
+    int32_t pair_token[kMaxPairsExt];
+    int32_t pair_src[kMaxPairsExt];
+};
+
+// One wave; lane p < P owns pair p with expert e_p.  Its compacted position
+// is the number of pairs ahead of it in (expert, pair index) order; a pair
+// that is its expert's first gets slot = number of distinct smaller experts.
+// The ids (at most PMAX) are read once with broadcast LDS loads.
+template <int PMAX>
+__device__ void compact_wave_t(int P, int K, RouteLds& r)
+{
+    const int lane = threadIdx.x & 63;
+    constexpr int NV = (PMAX + 3) / 4;
+    int4 ids4[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)       // unconditional: entries past P are ignored below
+        ids4[v] = *reinterpret_cast<const int4*>(r.ids + 4 * v);
+    const int e = (lane < P) ? r.ids[lane] : 0;
+    int pos = 0, same_before = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = 4 * v + u;
+            const bool in = q < P;
+            pos += in && ((eq[u] < e) || (eq[u] == e && q < lane));
+            same_before += in && (eq[u] == e) && (q < lane);
+        }
+    }
+    const bool first = lane < P && same_before == 0;
+    const uint64_t firsts = __ballot(first);
+    int slot = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = 4 * v + u;
+            slot += (q < P) && ((firsts >> q) & 1ull) && eq[u] < e;
+        }
+    }
+    if (lane < P) {
+        r.pair_token[pos] = lane / K;
+        r.pair_src[pos] = lane;
+        if (first) {
+            r.act_experts[slot] = e;
+            r.offsets[slot] = pos;
+        }
+    }
+    if (lane == 0) {
+        const int n = __popcll(firsts);
+        r.n_act = n;
+        r.offsets[n] = P;
+    }
+}
+
+__device__ void compact_wave(int P, int K, RouteLds& r)
+{
+    if (P <= 8) compact_wave_t<8>(P, K, r);
+    else if (P <= 16) compact_wave_t<16>(P, K, r);
+    else if (P <= 32) compact_wave_t<32>(P, K, r);
+    else compact_wave_t<64>(P, K, r);
+}
+
+__device__ void route_prologue(const RouteSrc& src, RouteLds& r)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int M = src.M, E = src.E, K = src.K, P = M * K;
+    if (src.logits != nullptr) {
+        for (int t = wave; t < M; t += nw)
+            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K);
+    } else {
+        for (int i = tid; i < P; i += blockDim.x) r.ids[i] = min(max(src.ids[i], 0), E - 1);   // clamped, never OOB
+    }
+    __syncthreads();
+    if (wave == 0) {
+        if (M == 1) {
+            // one token: its K experts are distinct, so the slots are the
+            // experts in ascending id and slot s holds exactly one pair
+            const int lane = tid & 63;
+            const int4 a4 = *reinterpret_cast<const int4*>(r.ids), b4 = *reinterpret_cast<const int4*>(r.ids + 4);
+            const int all[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+            const int e = r.ids[lane & (kMaxTopK - 1)];
+            int slot = 0;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) slot += (k < K) && all[k] < e;
+            if (lane < K) {
+                r.act_experts[slot] = e;
+                r.offsets[slot] = slot;
+                r.pair_token[slot] = 0;
+                r.pair_src[slot] = lane;
+            }
+            if (lane == 0) {
+                r.n_act = K;
+                r.offsets[K] = K;
+            }
+        } else {
+            compact_wave(P, K, r);
+        }
+        if (src.shared) {
+            // the shared expert's slot follows the routed ones: every token,
+            // pair row P + t (its weight, 1, is applied by the down kernel)
+            const int lane = tid & 63;
+            if (lane < M) {
+                r.pair_token[P + lane] = lane;
+                r.pair_src[P + lane] = P + lane;
+            }
+            if (lane == 0) {
+                const int n = r.n_act;
+                r.act_experts[n] = kSharedExpert;
+                r.offsets[n + 1] = P + M;
+                r.n_act = n + 1;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Writes the routing and compaction of one workgroup's prologue to global memory.
+__device__ void publish_route(const RouteLds& r, const RouteSrc& src, int32_t* ids_out, float* w_out,
+                              const Compaction& cp)
+{
+    const int tid = threadIdx.x, P = src.M * src.K, Pe = P + (src.shared ? src.M : 0);
+    if (tid < P) {
+        if (ids_out != nullptr) ids_out[tid] = r.ids[tid];
+        if (w_out != nullptr && src.logits != nullptr) w_out[tid] = r.w[tid];
+    }
+    if (tid < Pe) {
+        cp.pair_token[tid] = r.pair_token[tid];
+        cp.pair_src[tid] = r.pair_src[tid];
+    }
+    if (tid < r.n_act) cp.act_experts[tid] = r.act_experts[tid];
+    if (tid <= r.n_act) cp.offsets[tid] = r.offsets[tid];
+    if (tid == 0) *cp.n_act = r.n_act;
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a)
+{
+    __shared__ RouteLds r;
+    route_prologue(a.src, r);
+    publish_route(r, a.src, a.ids_out, a.w_out, a.cp);
+}
+
+// ---------------------------------------------------------------------------
+// Router: logits[t,e] = x[t] . Wr[e] in fp32 (exact bf16 products), one wave
+// per expert row with 16-byte loads; each workgroup also quantises a slice of
+// every token.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot_bf16x8(u32x4 x, u32x4 w, float acc)
+{
+    acc = fmaf(__uint_as_float(x.x << 16), __uint_as_float(w.x << 16), acc);
+    acc = fmaf(__uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(w.x & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(x.y << 16), __uint_as_float(w.y << 16), acc);
+    acc = fmaf(__uint_as_float(x.y & 0xFFFF0000u), __uint_as_float(w.y & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(x.z << 16), __uint_as_float(w.z << 16), acc);
+    acc = fmaf(__uint_as_float(x.z & 0xFFFF0000u), __uint_as_float(w.z & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(x.w << 16), __uint_as_float(w.w << 16), acc);
+    acc = fmaf(__uint_as_float(x.w & 0xFFFF0000u), __uint_as_float(w.w & 0xFFFF0000u), acc);
+    return acc;
+}
+
+template <int H, int MT>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a)
+{
+    constexpr int NCH = H / 8;                       // 16-byte chunks per row
+    constexpr int CPL = (NCH + kWave - 1) / kWave;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + wave;
+    auto valid = [&](int i) { return NCH % kWave == 0 || lane + kWave * i < NCH; };
+
+    // issue every load up front: the router row, each token's hidden state and
+    // this workgroup's quantisation slice
+    u32x4 wv[CPL];
+    if (e < a.E) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            if (valid(i)) wv[i] = load_stream((const u32x4*)(a.wr + (size_t)e * H) + lane + kWave * i);
+    }
+    u32x4 xv[MT][CPL];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            xv[t][i] = (t < a.M && valid(i)) ? *((const u32x4*)(a.x + (size_t)t * H) + lane + kWave * i)
+                                             : u32x4{0u, 0u, 0u, 0u};
+    const int per = (H + gridDim.x - 1) / gridDim.x;
+    const int kq = blockIdx.x * per + threadIdx.x;
+    const bool quant = a.act_q != nullptr && threadIdx.x < per && kq < H;
+    uint32_t xq[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xq[t] = (quant && t < a.M) ? a.x[(size_t)t * H + kq] : 0u;
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t >= a.M) continue;
+        if (e < a.E) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                if (valid(i)) acc = dot_bf16x8(xv[t][i], wv[i], acc);
+            const float sum = wave_sum(acc);
+            if (lane == 0) a.logits[(size_t)t * a.E + e] = sum;
+        }
+        if (a.act_q != nullptr) {
+            // every wave holds the whole token, so every wave finds the same amax
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].x << 16)), fabsf(__uint_as_float(xv[t][i].x & 0xFFFF0000u))));
+                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].y << 16)), fabsf(__uint_as_float(xv[t][i].y & 0xFFFF0000u))));
+                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].z << 16)), fabsf(__uint_as_float(xv[t][i].z & 0xFFFF0000u))));
+                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].w << 16)), fabsf(__uint_as_float(xv[t][i].w & 0xFFFF0000u))));
+            }
+            const float amax = wave_max(m);
+            const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+            if (quant) a.act_q[(size_t)t * H + kq] = (uint8_t)e4m3_encode(bf16_bits_to_f32(xq[t]) / s);
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.act_s[t] = s;
+        }
+    }
+
+}
+
+// ---------------------------------------------------------------------------
+// Fused gate/up GEMV.  A row of W13 is H/32 chunks of 16 code bytes, each
+// chunk exactly one E8M0 block.  LPR lanes share a row and each takes CPL
+// chunks (lane li takes chunks li, li+LPR, ...), so one load instruction of the
+// group covers LPR*16 contiguous bytes.  A lane holds the gate row r and the up
+// row I+r of one expert, so SiLU(g)*u is formed in registers.
+// ---------------------------------------------------------------------------
+template <int H, int I>
+struct GateUpGeom {
+    static constexpr int kChunks = H / 32;
+    static constexpr int kLanesPerRow = gate_up_lanes_per_row(H);
+    static constexpr int kChunksPerLane = kChunks / kLanesPerRow;
+    static constexpr int kRowsPerWave = kWave / kLanesPerRow;
+    static constexpr int kWaves = 4;
+    static constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
+    static_assert(kRowsPerBlock == gate_up_rows_per_block(H), "gate/up blocking");
+    static_assert(H % 32 == 0 && I % kRowsPerBlock == 0, "unsupported gate/up shape");
+    static constexpr int kBlocksPerExpert = I / kRowsPerBlock;
+};
+
+template <int H, int I, int MT>
+__global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
+{
+    using G = GateUpGeom<H, I>;
+    constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, BPE = G::kBlocksPerExpert;
+    __shared__ RouteLds rl;
+    __shared__ u32x4 act[MT * 4 * CH];          // [token][q][chunk] of 8 halves
+
+    const int M = a.src.M;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane % LPR, grp = lane / LPR;
+
+    // 0. every token's activations as f16 in LDS (independent of the routing,
+    //    so these loads overlap the routing prologue's); all loads first
+    constexpr int NST = (MT * (H / 8) + 255) / 256;
+    const int n8 = M * (H / 8);
+    u32x2 stg[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
+    // 1. routing, derived independently by every workgroup (the staging loads
+    //    above are in flight meanwhile); workgroup 0 publishes it for the down
+    //    kernel (and the caller)
+    route_prologue(a.src, rl);
+    if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+        const int idx = threadIdx.x + 256 * j;
+        if (idx < n8) {
+            const int t = idx / (H / 8), g8 = idx % (H / 8);
+            act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+        }
+    }
+    __syncthreads();
+    const int n_items = rl.n_act * BPE;
+
+    // 2. work items (selected expert, block of rows), strided over the grid;
+    //    the next item's weight loads are in flight while this one computes
+    struct Stage {
+        u32x4 wg[CPL], wu[CPL];
+        uint32_t sg[CPL], su[CPL];
+    };
+    auto issue = [&](int item, Stage& st) {
+        const int slot = item / BPE, rb = item % BPE;
+        const int e = rl.act_experts[slot];
+        const bool shared = e == kSharedExpert;
+        const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const uint8_t* w13e = shared ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
+        const uint8_t* s13e = shared ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * CH;
+        const u32x4* grow = (const u32x4*)(w13e + (size_t)r * (H / 2));
+        const u32x4* urow = grow + (size_t)I * CH;
+        const uint8_t* gsc = s13e + (size_t)r * CH;
+        const uint8_t* usc = gsc + (size_t)I * CH;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            st.wg[i] = load_stream(grow + li + LPR * i);
+            st.wu[i] = load_stream(urow + li + LPR * i);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            st.sg[i] = gsc[li + LPR * i];
+            st.su[i] = usc[li + LPR * i];
+        }
+    };
+    auto compute = [&](int item, Stage& st) {
+        const int slot = item / BPE, rb = item % BPE;
+        const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const int p0 = rl.offsets[slot];
+        const int nt = min(rl.offsets[slot + 1] - p0, MT);   // an expert has at most M <= MT tokens
+        float accg[MT], accu[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) accg[t] = accu[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = li + LPR * i;
+            half2_t hg[16], hu[16];
+            e2m1x8_to_half(st.wg[i].x, hg + 0);
+            e2m1x8_to_half(st.wg[i].y, hg + 4);
+            e2m1x8_to_half(st.wg[i].z, hg + 8);
+            e2m1x8_to_half(st.wg[i].w, hg + 12);
+            e2m1x8_to_half(st.wu[i].x, hu + 0);
+            e2m1x8_to_half(st.wu[i].y, hu + 4);
+            e2m1x8_to_half(st.wu[i].z, hu + 8);
+            e2m1x8_to_half(st.wu[i].w, hu + 12);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < nt) {
+                    const int tok = rl.pair_token[p0 + t];
+                    const u32x4 a0 = act[(tok * 4 + 0) * CH + c], a1 = act[(tok * 4 + 1) * CH + c];
+                    const u32x4 a2 = act[(tok * 4 + 2) * CH + c], a3 = act[(tok * 4 + 3) * CH + c];
+                    accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), st.sg[i]);
+                    accu[t] += ldexp_e8m0(block_dot(hu, a0, a1, a2, a3), st.su[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t < nt) {
+                accg[t] = group_sum<LPR>(accg[t]);
+                accu[t] = group_sum<LPR>(accu[t]);
+                const float sc = a.act_s[rl.pair_token[p0 + t]];
+                const float g = accg[t] * sc, u = accu[t] * sc;
+                if (li == 0) a.h[(size_t)rl.pair_src[p0 + t] * I + r] = g / (1.0f + expf(-g)) * u;
+            }
+        }
+    };
+
+    int item = blockIdx.x;
+    if (item >= n_items) return;
+    Stage s0, s1;
+    issue(item, s0);
+    for (;;) {
+        const int next = item + gridDim.x;
+        if (next < n_items) issue(next, s1);
+        compute(item, s0);
+        if (next >= n_items) break;
+        item = next;
+        const int after = item + gridDim.x;
+        if (after < n_items) issue(after, s0);
+        compute(item, s1);
+        if (after >= n_items) break;
+        item = after;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-(token, expert) FP8 requantisation of the intermediate, a wave per row
+// of I values: s2 = fl32(amax / 448) (1 for an all-zero row), and the codes
+// E4M3(h * fl32(1 / s2)).  (The codes may differ from E4M3(h / s2) only where
+// h / s2 lies within an ulp of a rounding midpoint.)  Lane l holds the I/64
+// consecutive elements starting at l * I/64.
+// ---------------------------------------------------------------------------
+template <int I>
+struct RequantRow {
+    static constexpr int PER = I / kWave;
+    static_assert(I % kWave == 0, "requantisation needs I % 64 == 0");
+    float v[PER];
+
+    __device__ __forceinline__ void load(const float* __restrict__ h, int p)
+    {
+        const float* row = h + (size_t)p * I + (threadIdx.x & 63) * PER;
+        if constexpr (PER % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < PER; i += 4) {
+                const float4 f = *reinterpret_cast<const float4*>(row + i);
+                v[i] = f.x; v[i + 1] = f.y; v[i + 2] = f.z; v[i + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[i] = row[i];
+        }
+    }
+    __device__ __forceinline__ float scale() const
+    {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = wave_max(m);
+        return (m == 0.0f) ? 1.0f : m / 448.0f;
+    }
+    // codes[j] holds elements 4j..4j+3 of this lane (PER % 4 == 0), or one
+    // code per entry otherwise
+    __device__ __forceinline__ void encode(float sc, uint32_t* codes) const
+    {
+        const float inv = 1.0f / sc;
+        if constexpr (PER % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < PER; i += 4)
+                codes[i / 4] = e4m3x4_encode(v[i] * inv, v[i + 1] * inv, v[i + 2] * inv, v[i + 3] * inv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) codes[i] = e4m3_encode(v[i] * inv);
+        }
+    }
+    static constexpr int NCODE = (PER % 4 == 0) ? PER / 4 : PER;
+};
+
+template <int I>
+__global__ __launch_bounds__(256) void requant_kernel(RequantArgs a)
+{
+    using R = RequantRow<I>;
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= a.P) return;
+    const int lane = threadIdx.x & 63;
+    R row;
+    row.load(a.h, p);
+    const float sc = row.scale();
+    uint32_t codes[R::NCODE];
+    row.encode(sc, codes);
+    uint8_t* dst = a.q2 + (size_t)p * I + lane * R::PER;
+    if constexpr (R::PER % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < R::NCODE; ++j) reinterpret_cast<uint32_t*>(dst)[j] = codes[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < R::NCODE; ++j) dst[j] = (uint8_t)codes[j];
+    }
+    if (lane == 0) a.s2[p] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Down GEMV + combine.  A workgroup owns RPB output rows for every token; its
+// 8 waves split the selected experts (wave w takes slots w, w+8, ...), each
+// accumulating per-token partial sums in a fixed slot order; the waves' sums
+// are then added in wave order.  The FP8 intermediate of every pair is held
+// once per workgroup as f16 in LDS.
+// ---------------------------------------------------------------------------
+template <int H, int I>
+struct DownGeom {
+    static constexpr int kChunks = I / 32;
+    static constexpr int kLanesPerRow = down_lanes_per_row(I);
+    static constexpr int kChunksPerLane = kChunks / kLanesPerRow;
+    static constexpr int kRowsPerBlock = kWave / kLanesPerRow;
+    static_assert(kRowsPerBlock == down_rows_per_block(I), "down blocking");
+    static constexpr int kWaves = 8;
+    static_assert(I % 32 == 0 && H % kRowsPerBlock == 0, "unsupported down shape");
+};
+
+template <int H, int I, int MT, bool FROM_H>
+__global__ __launch_bounds__(512) void down_kernel(DownArgs a)
+{
+    using G = DownGeom<H, I>;
+    constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, RPB = G::kRowsPerBlock;
+    extern __shared__ u32x4 q2h[];                 // [pair][q][chunk] of 8 halves
+    __shared__ float red[G::kWaves][RPB][MT];
+    __shared__ float s2l[kMaxPairsExt];
+
+    const bool shared = a.sh.w2 != nullptr;
+    const int P = a.M * a.K, Pe = P + (shared ? a.M : 0);   // routed pairs, plus the shared expert's rows
+    const int n_act = min(*a.cp.n_act, min(a.E, P) + (shared ? 1 : 0));
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane % LPR, grp = lane / LPR;
+    const int n = blockIdx.x * RPB + grp;
+
+    auto load_slot = [&](int slot, u32x4* wv, uint32_t* sv) {
+        const int ea = a.cp.act_experts[slot];
+        const bool sh = shared && ea == kSharedExpert;
+        const int e = min(max(ea, 0), a.E - 1);
+        const u32x4* row = (const u32x4*)((sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2)) + (size_t)n * (I / 2));
+        const uint8_t* sc = (sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH) + (size_t)n * CH;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) wv[i] = load_stream(row + li + LPR * i);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) sv[i] = sc[li + LPR * i];
+    };
+
+    // The intermediate in LDS as f16.  From h: a wave per (token, expert) row
+    // requantises it (the same arithmetic as requant_kernel), which every
+    // workgroup repeats so that no workgroup waits for another; the rows'
+    // loads go out before the weight stream so they are not queued behind it.
+    using R = RequantRow<I>;
+    constexpr int RB = MT < 4 ? MT : 4;            // rows per wave held at once
+    R rows[RB];
+    if constexpr (FROM_H) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(wave + G::kWaves * j, Pe - 1));
+    }
+    int slot = wave;
+    u32x4 wv[CPL];
+    uint32_t sv[CPL];
+    if (slot < n_act) load_slot(slot, wv, sv);
+
+    if constexpr (FROM_H) {
+        _Float16* q16 = reinterpret_cast<_Float16*>(q2h);
+        const bool tap = blockIdx.x == 0 && a.q2_out != nullptr;
+        for (int base = 0; base < Pe; base += G::kWaves * RB) {
+            if (base > 0) {
+#pragma unroll
+                for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(base + wave + G::kWaves * j, Pe - 1));
+            }
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const int p = base + wave + G::kWaves * j;
+                if (p >= Pe) break;
+                const float sc = rows[j].scale();
+                uint32_t codes[R::NCODE];
+                rows[j].encode(sc, codes);
+                const int k0 = lane * R::PER;
+                if constexpr (R::PER % 4 == 0) {
+#pragma unroll
+                    for (int c4 = 0; c4 < R::NCODE; ++c4) {
+                        const int k = k0 + 4 * c4;       // 4 consecutive elements, inside one group of 8
+                        uint2 hv2;
+                        hv2.x = e4m3x2_to_half2<false>(codes[c4]);
+                        hv2.y = e4m3x2_to_half2<true>(codes[c4]);
+                        *reinterpret_cast<uint2*>(q16 + ((p * 4 + ((k & 31) >> 3)) * CH + (k >> 5)) * 8 + (k & 7)) = hv2;
+                        if (tap) reinterpret_cast<uint32_t*>(a.q2_out + (size_t)p * I + k0)[c4] = codes[c4];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < R::NCODE; ++i) {
+                        const int k = k0 + i;
+                        q16[((p * 4 + ((k & 31) >> 3)) * CH + (k >> 5)) * 8 + (k & 7)] = (_Float16)e4m3_decode(codes[i]);
+                        if (tap) a.q2_out[(size_t)p * I + k] = (uint8_t)codes[i];
+                    }
+                }
+                if (lane == 0) {
+                    s2l[p] = sc;
+                    if (tap && a.s2_out != nullptr) a.s2_out[p] = sc;
+                }
+            }
+        }
+    } else {
+        constexpr int NST = (MT * 8 * (I / 8) + 511) / 512;
+        const int n8 = P * (I / 8);
+        u32x2 stg[NST];
+#pragma unroll
+        for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.q2)[min((int)threadIdx.x + 512 * j, n8 - 1)];
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+            const int idx = threadIdx.x + 512 * j;
+            if (idx < n8) {
+                const int p = idx / (I / 8), g8 = idx % (I / 8);
+                q2h[(p * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+            }
+        }
+        for (int p = threadIdx.x; p < P; p += blockDim.x) s2l[p] = a.s2[p];
+    }
+    __syncthreads();
+
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+    for (; slot < n_act; slot += G::kWaves) {
+        u32x4 nwv[CPL];
+        uint32_t nsv[CPL];
+        const int nslot = slot + G::kWaves;
+        if (nslot < n_act) load_slot(nslot, nwv, nsv);
+        half2_t hw[CPL * 16];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            e2m1x8_to_half(wv[i].x, hw + 16 * i + 0);
+            e2m1x8_to_half(wv[i].y, hw + 16 * i + 4);
+            e2m1x8_to_half(wv[i].z, hw + 16 * i + 8);
+            e2m1x8_to_half(wv[i].w, hw + 16 * i + 12);
+        }
+        const int q0 = min(max(a.cp.offsets[slot], 0), Pe), q1 = min(a.cp.offsets[slot + 1], Pe);
+        for (int qq = q0; qq < q1; ++qq) {
+            const int p = min(max(a.cp.pair_src[qq], 0), Pe - 1);
+            const int tok = a.cp.pair_token[qq];
+            float d = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = li + LPR * i;
+                const u32x4 a0 = q2h[(p * 4 + 0) * CH + c], a1 = q2h[(p * 4 + 1) * CH + c];
+                const u32x4 a2 = q2h[(p * 4 + 2) * CH + c], a3 = q2h[(p * 4 + 3) * CH + c];
+                d += ldexp_e8m0(block_dot(hw + 16 * i, a0, a1, a2, a3), sv[i]);
+            }
+            d = group_sum<LPR>(d);
+            const float coef = (p < P ? a.topk_w[p] : 1.0f) * s2l[p];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                if (t == tok) acc[t] = fmaf(coef, d, acc[t]);
+        }
+        if (nslot < n_act) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                wv[i] = nwv[i];
+                sv[i] = nsv[i];
+            }
+        }
+    }
+    if (li == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave][grp][t] = acc[t];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < RPB * a.M; idx += blockDim.x) {
+        const int row = idx % RPB, t = idx / RPB;
+        float s = red[0][row][t];
+#pragma unroll
+        for (int w = 1; w < G::kWaves; ++w) s += red[w][row][t];
+        a.out[(size_t)t * H + blockIdx.x * RPB + row] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small utility kernels.
+// ---------------------------------------------------------------------------
+__global__ void fp8_encode_range_kernel(uint32_t first, int64_t n, uint8_t* __restrict__ q)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        q[i] = (uint8_t)e4m3_encode(__uint_as_float(first + (uint32_t)i));
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+}  // namespace moe

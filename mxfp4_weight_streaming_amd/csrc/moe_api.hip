@@ -10,7 +10,7 @@
 
 namespace {
 
-thread_local char g_last_error[512] = "";
+thread_local char g_last_error[4096] = "";
 
 moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 moe_status fail(moe_status st, const char* fmt, ...)
@@ -36,6 +36,9 @@ int token_bound(int M)
     return mt;
 }
 
+// M above the GEMV bound takes the chunk path (grouped MFMA contractions).
+bool chunked(int32_t M) { return M > moe::kMaxGemvTokens; }
+
 // Shape checks shared by every entry point.
 moe_status check_shape(const moe_shape* s, int32_t M)
 {
@@ -54,18 +57,25 @@ moe_status check_shape(const moe_shape* s, int32_t M)
     if (s->num_experts > moe::kMaxExperts)
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E (%d) above %d is not compiled", s->num_experts, moe::kMaxExperts);
     if (!moe::gemv_shape_supported(s->hidden, s->inter))
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "(H=%d, I=%d) is not a compiled shape; compiled: (256,64), (2560,768)",
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                    "(H=%d, I=%d) has no kernels on this device: compiled in are (256,64) and (2560,768); other "
+                    "shapes need moe_jit_load first",
                     s->hidden, s->inter);
     if (M > moe::kMaxChunkTokens)
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "M=%d above %d tokens is not compiled", M, moe::kMaxChunkTokens);
-    if (M > moe::kMaxGemvTokens && !moe::chunk_shape_supported(s->hidden, s->inter, s->num_experts))
+    if (!chunked(M) && (size_t)(M * s->topk + M) * s->inter * 2 > moe::kMaxDynamicLds)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                    "the down kernel holds the %d x %d FP8 intermediate rows of M=%d tokens in LDS as f16 (%zu "
+                    "bytes), above the %zu a workgroup can have",
+                    M * s->topk + M, s->inter, M, (size_t)(M * s->topk + M) * s->inter * 2, moe::kMaxDynamicLds);
+    if (M > moe::kMaxGemvTokens && s->num_experts % 16 != 0)
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "the chunk path (M > %d) needs E %% 16 == 0 (E=%d)",
                     moe::kMaxGemvTokens, s->num_experts);
+    if (M > moe::kMaxGemvTokens && !moe::chunk_shape_supported(s->hidden, s->inter, s->num_experts))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "(H=%d, I=%d) has no chunk-path kernels (M > %d)", s->hidden, s->inter,
+                    moe::kMaxGemvTokens);
     return MOE_OK;
 }
-
-// M above the GEMV bound takes the chunk path (grouped MFMA contractions).
-bool chunked(int32_t M) { return M > moe::kMaxGemvTokens; }
 
 moe_status check_ws(const moe_shape* s, int32_t M, void* ws, size_t ws_bytes)
 {
@@ -546,7 +556,10 @@ moe_status moe_lm_head_forward(const uint16_t* x_bf16, int32_t M, const uint8_t*
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "the LM-head GEMV is compiled for up to %d tokens (M=%d)",
                     moe::kMaxGemvTokens, M);
     if (!moe::lm_head_shape_supported(hidden))
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d is not a compiled LM-head shape; compiled: 512, 2560", hidden);
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                    "hidden %d has no LM-head kernel on this device: compiled in are 512 and 2560; other sizes "
+                    "(multiples of 256 up to 4096) need moe_jit_load of a layer shape with that hidden size first",
+                    hidden);
     hipError_t e = moe::launch_lm_head_gemv(hidden, token_bound(M), x_bf16, M, q, scale, vocab, logits,
                                             static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "lm-head GEMV launch");
@@ -564,16 +577,70 @@ moe_status moe_path_info(const moe_shape* shape, int32_t M, char* buf, size_t le
 {
     moe_status st = check_shape(shape, M);
     if (buf != nullptr && len > 0) {
-        if (st != MOE_OK)
+        char names[1024];
+        if (st != MOE_OK) {
             snprintf(buf, len, "unsupported: %s", g_last_error);
-        else if (chunked(M))
-            snprintf(buf, len, "chunk path, M=%d, E=%d, K=%d: %s", M, shape->num_experts, shape->topk,
-                     moe::chunk_kernel_names(shape->hidden, shape->inter));
-        else
+        } else if (chunked(M)) {
+            moe::chunk_kernel_names(shape->hidden, shape->inter, names, sizeof names);
+            snprintf(buf, len, "chunk path, M=%d, E=%d, K=%d: %s", M, shape->num_experts, shape->topk, names);
+        } else {
+            moe::kernel_names(shape->hidden, shape->inter, names, sizeof names);
             snprintf(buf, len, "gemv path, M=%d (token bound %d), E=%d, K=%d: %s", M, token_bound(M),
-                     shape->num_experts, shape->topk, moe::kernel_names(shape->hidden, shape->inter, token_bound(M)));
+                     shape->num_experts, shape->topk, names);
+        }
     }
     return st;
+}
+
+static moe_status jit_status(moe::JitStatus st, const std::string& err)
+{
+    switch (st) {
+        case moe::JitStatus::Ok: return MOE_OK;
+        case moe::JitStatus::BadShape:
+        case moe::JitStatus::BadArch: return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s", err.c_str());
+        case moe::JitStatus::CacheIo:
+        case moe::JitStatus::Compile: return fail(MOE_ERR_JIT, "%s", err.c_str());
+        case moe::JitStatus::Load: return fail(MOE_ERR_HIP, "%s", err.c_str());
+    }
+    return fail(MOE_ERR_JIT, "%s", err.c_str());
+}
+
+static void fill_report(moe_jit_report* r, const moe::JitReport& j)
+{
+    if (r == nullptr) return;
+    r->from_cache = j.from_cache ? 1 : 0;
+    r->has_chunk_path = j.chunk ? 1 : 0;
+    r->has_lm_head = j.lm_head ? 1 : 0;
+    r->num_kernels = j.kernels;
+    r->seconds = j.seconds;
+    snprintf(r->cache_file, sizeof r->cache_file, "%s", j.file);
+}
+
+moe_status moe_jit_build(const moe_shape* shape, const char* arch, const char* cache_dir, moe_jit_report* report)
+{
+    if (shape == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (arch == nullptr) return fail(MOE_ERR_INVALID_ARG, "arch is NULL");
+    moe::JitReport j;
+    std::string err;
+    const moe::JitStatus st = moe::jit_build(shape->hidden, shape->inter, arch, cache_dir, &j, &err);
+    fill_report(report, j);
+    return jit_status(st, err);
+}
+
+moe_status moe_jit_load(const moe_shape* shape, const char* cache_dir, int32_t prefer, moe_jit_report* report)
+{
+    if (shape == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    moe::JitReport j;
+    std::string err;
+    const moe::JitStatus st = moe::jit_load(shape->hidden, shape->inter, cache_dir, prefer != 0, &j, &err);
+    fill_report(report, j);
+    return jit_status(st, err);
+}
+
+int32_t moe_jit_unload(const moe_shape* shape)
+{
+    if (shape == nullptr) return 0;
+    return moe::jit_unload(shape->hidden, shape->inter);
 }
 
 const char* moe_status_string(moe_status status)
@@ -585,6 +652,7 @@ const char* moe_status_string(moe_status status)
         case MOE_ERR_ALIGNMENT: return "misaligned pointer";
         case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_JIT: return "run-time compilation or its cache failed";
     }
     return "unknown status";
 }

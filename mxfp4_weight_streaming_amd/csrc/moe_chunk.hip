@@ -1,191 +1,13 @@
-// moe_chunk.hip -- gfx950 kernels of the MoE layer for chunks of 9..2048
-// tokens (a prefill chunk, or a large verify batch).
-//
-// At these token counts every expert is picked by several tokens, so the
-// expert layers are grouped contractions: per active expert e, the FP8 rows of
-// its tokens times the MXFP4 weights of e.  They run on the scaled FP4xFP8
-// matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): the E8M0 block scales of
-// the weights enter the instruction directly, the per-token fp32 activation
-// and intermediate scales are applied in the epilogues, and the router weight
-// in the combine.  The
-// pages profile MoE decode as bound by reading expert weights ([EN] "Why is
-// MoE decoding on DGX Spark memory-bound?"); here too each weight byte is read
-// from HBM once per call, by the wave that owns its 16 rows.
-//
-// A chunk is eight kernels on one stream:
-//   chunk_router_kernel   bf16 MFMA router GEMM, fp32 logits
-//   quant_kernel          per-token FP8 activations (shared with the decode path)
-//   chunk_topk_kernel     one wave per token: top-K and renormalised weights
-//   sort_pairs_kernel     one workgroup: (expert, pair) bitonic sort in LDS ->
-//                         active experts, per-expert offsets, pair lists
-//   chunk_gate_up_kernel  per (expert, 32 intermediate rows): gate and up
-//                         tiles on MFMA, K split over the workgroup's waves,
-//                         SiLU(gate)*up epilogue -> h fp32
-//   requant_kernel        per (token, expert) FP8 requantisation of h
-//   chunk_down_kernel     per (expert, 128 output rows): down tiles on MFMA,
-//                         epilogue scales by s2 -> y
-//   combine_kernel        out[t] = sum over the token's K pairs of w * y, in
-//                         selection order (no float atomics)
-//
-// Operand layouts of the 16x16x128 scaled MFMA (lane l, r = l % 16,
-// g = l / 16), established by direct tests on gfx950:
-//   FP8 operand: row r; bytes 0..15 hold K = 16g..16g+15 and bytes 16..31
-//                hold K = 64+16g..64+16g+15.
-//   FP4 operand: row r; the 32 nibbles of dwords 0..3 hold K = 32g..32g+31,
-//                low nibble first (the MX byte order).
-//   Scales:      lane l supplies the E8M0 code of row r, K block g.
-//   Result:      lane l holds C[4g + i][r], i = 0..3.
-// bf16 16x16x32 MFMA: row r holds K = 8g..8g+7 of each operand; same result
-// layout.
-//   [EN] = "NVIDIA Shows 3 Ways to Speed Up MoE Inference on DGX Spark,
-//          Lifting Ling-3.0-flash Throughput 42.5%"
+// moe_chunk.hip -- host launchers of the chunk-path kernels in
+// chunk_kernels.hpp (9..2048 tokens).
 #include <hip/hip_ext.h>
+#include <stdio.h>
 
-#include <type_traits>
-#include <utility>
-
-#include "device_common.hpp"
+#include "chunk_kernels.hpp"
+#include "kernel_table.hpp"
 #include "moe_internal.hpp"
-#include "topk_wave.hpp"
 
 namespace moe {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop
-// index, for operands that must be constants).
-template <int N, typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>)
-{
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f)
-{
-    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
-
-// C += A(FP8, unit scale) * B(FP4, E8M0 scale code sb)
-__device__ __forceinline__ f32x4 mfma_fp8_fp4(i32x8 a, i32x8 b, f32x4 c, int sb)
-{
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
-}
-
-// The same with the B scale code taken from byte SEL of a packed register.
-template <int SEL>
-__device__ __forceinline__ f32x4 mfma_fp8_fp4_sel(i32x8 a, i32x8 b, f32x4 c, int packed)
-{
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, SEL, packed);
-}
-
-// Scale code q of a lane, packed four per register, applied with op_sel.
-template <int Q>
-__device__ __forceinline__ f32x4 mfma_packed_scale(i32x8 a, i32x8 b, f32x4 c, const int* packed)
-{
-    return mfma_fp8_fp4_sel<Q % 4>(a, b, c, packed[Q / 4]);
-}
-
-__device__ __forceinline__ i32x8 fp8_operand(u32x4 lo, u32x4 hi)
-{
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-__device__ __forceinline__ i32x8 fp4_operand(u32x4 v)
-{
-    return i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-}
-
-// ---------------------------------------------------------------------------
-// Router: logits[t, e] = sum_k x[t, k] * Wr[e, k] on bf16 MFMA with fp32
-// accumulation.  One workgroup per 16x16 (token, expert) tile; its 8 waves
-// take K slices of H/8 with every load issued up front, and the slices are
-// added in LDS in wave order.
-// ---------------------------------------------------------------------------
-constexpr int kRouterWaves = 8;
-
-template <int H>
-__global__ __launch_bounds__(kRouterWaves * kWave) void chunk_router_kernel(ChunkRouterArgs a)
-{
-    constexpr int KW = H / kRouterWaves;                 // K slice of a wave
-    constexpr int NS = KW / 32;                          // MFMA steps per slice
-    static_assert(H % (kRouterWaves * 32) == 0, "router slice must be a whole number of MFMA steps");
-    __shared__ float red[kRouterWaves][4][kWave];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const int tiles_e = a.E >> 4;
-    const int tm = blockIdx.x / tiles_e, te = blockIdx.x - tm * tiles_e;
-    const int m = min(tm * 16 + r, a.M - 1);            // ragged tail: repeat the last token
-    const uint16_t* xr = a.x + (size_t)m * H + w * KW + 8 * g;
-    const uint16_t* wr = a.wr + (size_t)(te * 16 + r) * H + w * KW + 8 * g;
-    bf16x8 av[NS], bv[NS];
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-        av[q] = *reinterpret_cast<const bf16x8*>(xr + 32 * q);
-        bv[q] = *reinterpret_cast<const bf16x8*>(wr + 32 * q);
-    }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int q = 0; q < NS; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[q], bv[q], acc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[w][i][lane] = acc[i];
-    __syncthreads();
-    if (threadIdx.x < 256) {                             // thread (i, l): C[4 (l >> 4) + i][l & 15]
-        const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
-        float v = red[0][i][l];
-#pragma unroll
-        for (int u = 1; u < kRouterWaves; ++u) v += red[u][i][l];
-        const int row = tm * 16 + 4 * (l >> 4) + i;
-        if (row < a.M) a.logits[(size_t)row * a.E + te * 16 + (l & 15)] = v;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Top-K and weights, one wave per token.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
-{
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.M) return;                              // whole wave; no barrier follows
-    topk_wave(a.logits + (size_t)t * a.E, a.E, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K);
-}
-
-// ---------------------------------------------------------------------------
-// Expert-major ordering of the M*K (token, slot) pairs by one workgroup.  The
-// pairs of an expert end up contiguous and in ascending token order (the
-// decode path's compaction order); active experts get slots in ascending id.
-// When every token's K ids are distinct (always so for routed ids), each
-// expert gets an M-bit token mask in LDS and a pair's rank inside its expert
-// is a popcount of the mask below its token.  Caller ids that repeat an
-// expert inside one token take a bitonic sort of (expert << 16 | pair) keys.
-// The rows of every slot are then cut into chunks of at most kChunkRows rows
-// for the grouped kernels, 4-tile chunks first, then 3-, 2- and 1-tile ones.
-// ---------------------------------------------------------------------------
-constexpr int kSortThreads = 1024;
-
-// Exclusive prefix sum of one value per thread over the workgroup, in thread
-// order; every thread must call it.
-__device__ int block_excl_scan(int v, int* tmp, int& total)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) tmp[w] = x;
-    __syncthreads();
-    int base = 0, tot = 0;
-    for (int i = 0; i < kSortThreads / kWave; ++i) {
-        const int t = tmp[i];
-        base += (i < w) ? t : 0;
-        tot += t;
-    }
-    __syncthreads();
-    total = tot;
-    return base + x - v;
-}
 
 size_t sort_lds_bytes(int M, int K, int E)
 {
@@ -196,456 +18,50 @@ size_t sort_lds_bytes(int M, int K, int E)
     return 4 * (mask_words > (size_t)NP ? mask_words : (size_t)NP);
 }
 
-__global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
-{
-    extern __shared__ uint32_t sh[];                     // token masks, or sort keys
-    __shared__ int32_t cnt[kMaxExperts];
-    __shared__ int32_t pre[kMaxExperts];
-    __shared__ int32_t tmp[kSortThreads / kWave];
-    __shared__ int32_t dup;
-    const int P = a.M * a.K, K = a.K, E = a.E, W = (a.M + 31) >> 5;
-    const int tid = threadIdx.x;
-    auto clamp_e = [&](int e) { return e < 0 ? 0 : (e >= E ? E - 1 : e); };
-    if (tid == 0) dup = 0;
-    for (int e = tid; e < kMaxExperts; e += kSortThreads) cnt[e] = 0;
-    for (int i = tid; i < E * W; i += kSortThreads) sh[i] = 0u;
-    __syncthreads();
-    for (int p = tid; p < P; p += kSortThreads) {
-        const int t = p / K, j = p - t * K;
-        const int e = clamp_e(a.ids[p]);
-        bool d = false;
-        for (int jj = 0; jj < j; ++jj) d |= clamp_e(a.ids[t * K + jj]) == e;
-        if (d) dup = 1;
-        atomicOr(&sh[e * W + (t >> 5)], 1u << (t & 31));
-        atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-    // expert offsets and slots (one thread per expert; thread E stands for the
-    // shared expert, whose M rows follow the routed pairs in one more slot)
-    const bool virt = a.shared != 0 && tid == E;
-    const int c = (tid < E) ? cnt[tid] : (virt ? a.M : 0);
-    int total_pairs = 0, n_act = 0;
-    const int off_e = block_excl_scan(c, tmp, total_pairs);
-    const int slot_e = block_excl_scan(c > 0 ? 1 : 0, tmp, n_act);
-    const int rec_e = virt ? kSharedExpert : tid;
-    if (tid < E) pre[tid] = off_e;
-    if (c > 0) {
-        a.cp.act_experts[slot_e] = rec_e;
-        a.cp.offsets[slot_e] = off_e;
-    }
-    if (tid == 0) {
-        *a.cp.n_act = n_act;
-        a.cp.offsets[n_act] = total_pairs;
-    }
-    if (a.shared != 0) {
-        for (int t = tid; t < a.M; t += kSortThreads) {
-            a.cp.pair_token[P + t] = t;
-            a.cp.pair_src[P + t] = P + t;
-            a.pos_of[P + t] = P + t;
-        }
-    }
-    __syncthreads();
-    if (dup == 0) {
-        for (int p = tid; p < P; p += kSortThreads) {
-            const int t = p / K;
-            const int e = clamp_e(a.ids[p]);
-            const uint32_t* mrow = sh + e * W;
-            int rank = __popc(mrow[t >> 5] & ((1u << (t & 31)) - 1u));
-            for (int w = 0; w < (t >> 5); ++w) rank += __popc(mrow[w]);
-            const int pos = pre[e] + rank;
-            a.cp.pair_token[pos] = t;
-            a.cp.pair_src[pos] = p;
-            a.pos_of[p] = pos;
-        }
-    } else {
-        int NP = 64;
-        while (NP < P) NP <<= 1;
-        __syncthreads();
-        for (int i = tid; i < NP; i += kSortThreads)
-            sh[i] = (i < P) ? (((uint32_t)clamp_e(a.ids[i]) << 16) | (uint32_t)i) : 0xFFFFFFFFu;
-        __syncthreads();
-        for (int size = 2; size <= NP; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < NP / 2; i += kSortThreads) {
-                    const int lo = 2 * i - (i & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool ascending = (lo & size) == 0;
-                    const uint32_t x = sh[lo], y = sh[hi];
-                    if ((x > y) == ascending) {
-                        sh[lo] = y;
-                        sh[hi] = x;
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        for (int pos = tid; pos < P; pos += kSortThreads) {
-            const int p = (int)(sh[pos] & 0xFFFFu);
-            a.cp.pair_token[pos] = p / K;
-            a.cp.pair_src[pos] = p;
-            a.pos_of[p] = pos;
-        }
-    }
-    // chunk list, from the expert's own thread (its count c and slot_e): its
-    // 4-tile chunks first, then its last chunk in the group of its tile count
-    const int rem = c % kChunkRows;
-    const int full = c / kChunkRows + (rem > 3 * 16 ? 1 : 0);
-    const int last_tiles = (rem > 0 && rem <= 3 * 16) ? (rem + 15) / 16 : 0;
-    int n4 = 0, n3 = 0, n2 = 0, n1 = 0;
-    const int at4 = block_excl_scan(full, tmp, n4);
-    const int at3 = block_excl_scan(last_tiles == 3 ? 1 : 0, tmp, n3);
-    const int at2 = block_excl_scan(last_tiles == 2 ? 1 : 0, tmp, n2);
-    const int at1 = block_excl_scan(last_tiles == 1 ? 1 : 0, tmp, n1);
-    if (c > 0) {
-        for (int k = 0; k < full; ++k) {
-            const int rows = c - k * kChunkRows;
-            a.chunks.rec[at4 + k] = make_int4(rec_e, off_e + k * kChunkRows, rows < kChunkRows ? rows : kChunkRows, 0);
-        }
-        if (last_tiles > 0) {
-            const int idx = n4 + (last_tiles == 3 ? at3 : last_tiles == 2 ? n3 + at2 : n3 + n2 + at1);
-            a.chunks.rec[idx] = make_int4(rec_e, off_e + full * kChunkRows, rem, 0);
-        }
-    }
-    const int n_chunks = n4 + n3 + n2 + n1;
-    for (int i = n_chunks + tid; i < a.chunks.C; i += kSortThreads) a.chunks.rec[i] = make_int4(0, 0, 0, 0);
-    if (tid == 0) *a.chunks.n_chunks = n_chunks;
-}
-
 // ---------------------------------------------------------------------------
-// Gate/up: workgroup (chunk, jq) owns the kGuRows = 16 NJ intermediate rows
-// j = kGuRows jq .. +kGuRows-1 of the chunk's expert, for both the gate (rows j)
-// and the up (rows I + j) projection, over the chunk's (at most 64) tokens.
-// Its waves split K = H into KSPLIT slices: each wave issues all the weight
-// loads of its slice at once (NJ n-tiles of gate and of up, so one activation
-// operand feeds 2 NJ MFMAs), together with the token ids of every tile of the
-// chunk; the block scales of the workgroup's rows are read with full-width
-// loads into LDS.  The 16-token tiles then run with the next tile's
-// activations loading while the current one is reduced; the slices' partial
-// sums are added in LDS in a fixed wave order, where SiLU(g)*u and the
-// per-token activation scale are applied.
+// Ahead-of-time instantiations: (H, I) in {(256, 64), (2560, 768)}.  Other
+// shapes run kernels compiled at run time.
 // ---------------------------------------------------------------------------
-template <int H>
-struct ChunkSplit {
-    static constexpr int KS = H / 128;                  // 128-deep k-steps
-    static constexpr int KSPLIT = KS >= 4 ? 4 : KS;     // waves with a K slice
-    static constexpr int KQ = KS / KSPLIT;              // k-steps per slice
-    static_assert(H % 128 == 0 && KS % KSPLIT == 0, "unsupported H for the chunk gate/up");
-};
+#define MOE_CHUNK_SHAPE(H, I)                                                                    \
+    {key_chunk_router(H), (const void*)chunk_router_kernel<H>},                                 \
+    {key_chunk_gate_up(H, I), (const void*)chunk_gate_up_kernel<H, I>},                         \
+    {key_chunk_down(H, I, false), (const void*)chunk_down_kernel<H, I, false>},                 \
+    {key_chunk_down(H, I, true), (const void*)chunk_down_kernel<H, I, true>},                   \
+    {key_combine(H), (const void*)combine_kernel<H>},
 
-constexpr int kChunkTiles = kChunkRows / 16;
-constexpr int kGuNJ = 2;                                // 16-row n-tiles per wave and matrix
-constexpr int kGuRows = 16 * kGuNJ;
+const AotKernel kChunkAot[] = {MOE_CHUNK_SHAPE(256, 64) MOE_CHUNK_SHAPE(2560, 768)};
+const int kChunkAotCount = (int)(sizeof(kChunkAot) / sizeof(kChunkAot[0]));
+#undef MOE_CHUNK_SHAPE
 
-// Copies `bytes` (a multiple of 16) from global to LDS with 16-byte loads by
-// the whole workgroup of 256 threads.
-__device__ __forceinline__ void copy_to_lds(uint8_t* dst, const uint8_t* src, int bytes)
-{
-    for (int i = threadIdx.x * 16; i < bytes; i += 256 * 16)
-        *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(src + i);
-}
-
-template <int H, int I>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void chunk_gate_up_kernel(
-    ChunkGateUpArgs a)
-{
-    using G = ChunkSplit<H>;
-    constexpr int KQ = G::KQ, NJ = kGuNJ, SROW = H / 32;
-    static_assert(I % kGuRows == 0 && (kGuRows * SROW) % 16 == 0, "chunk gate/up row blocking");
-    __shared__ float red[4][NJ][2][4][kWave];            // [wave][n-tile][gate/up][i][lane]
-    __shared__ alignas(16) uint8_t sc_lds[2][kGuRows * SROW];   // [gate/up][row][block]
-    __shared__ float tok_scale[16];
-    const int jq = blockIdx.x % (I / kGuRows);
-    const int4 rec = a.chunks.rec[blockIdx.x / (I / kGuRows)];
-    const int e = rec.x, off = rec.y, n = rec.z;
-    if (n == 0) return;                                 // whole workgroup: past the last chunk
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const bool has_k = w < G::KSPLIT;
-    const int ks0 = (has_k ? w : 0) * KQ;
-    const int j0 = jq * kGuRows;
-    const uint8_t* w13e = e == kSharedExpert ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
-    i32x8 bg[NJ][KQ], bu[NJ][KQ];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-        const uint8_t* wg = w13e + (size_t)(j0 + 16 * nj + r) * (H / 2) + 16 * g;
-        const uint8_t* wu = wg + (size_t)I * (H / 2);
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            bg[nj][q] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wg + (ks0 + q) * 64)));
-            bu[nj][q] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wu + (ks0 + q) * 64)));
-        }
-    }
-    int tok[kChunkTiles];
-#pragma unroll
-    for (int tt = 0; tt < kChunkTiles; ++tt) {
-        const int row = tt * 16 + r;
-        tok[tt] = a.cp.pair_token[off + (row < n ? row : n - 1)];
-    }
-    const uint8_t* s13e = e == kSharedExpert ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * SROW;
-    copy_to_lds(sc_lds[0], s13e + (size_t)j0 * SROW, kGuRows * SROW);
-    copy_to_lds(sc_lds[1], s13e + (size_t)(I + j0) * SROW, kGuRows * SROW);
-    u32x4 alo[KQ], ahi[KQ];
-    float s_row = 0.0f;
-    auto load_tile = [&](int t) {
-        const uint8_t* ar = a.act_q + (size_t)t * H + ks0 * 128 + 16 * g;
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            alo[q] = *reinterpret_cast<const u32x4*>(ar + q * 128);
-            ahi[q] = *reinterpret_cast<const u32x4*>(ar + q * 128 + 64);
-        }
-        s_row = a.act_s[t];
-    };
-    load_tile(tok[0]);
-    __syncthreads();                                     // block scales in LDS
-    constexpr int NP = (KQ + 3) / 4;                    // packed scale registers per n-tile
-    int sg[NJ][NP], su[NJ][NP];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-#pragma unroll
-        for (int u = 0; u < NP; ++u) sg[nj][u] = su[nj][u] = 0;
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            const int idx = (16 * nj + r) * SROW + (ks0 + q) * 4 + g;
-            sg[nj][q / 4] |= (int)sc_lds[0][idx] << (8 * (q % 4));
-            su[nj][q / 4] |= (int)sc_lds[1][idx] << (8 * (q % 4));
-        }
-    }
-    const int ntiles = (n + 15) / 16;
-#pragma unroll
-    for (int tile = 0; tile < kChunkTiles; ++tile) {
-        if (tile >= ntiles) break;
-        f32x4 accg[NJ], accu[NJ];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            accg[nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            accu[nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        static_for<KQ>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const i32x8 av = fp8_operand(alo[q], ahi[q]);
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj) {
-                accg[nj] = mfma_packed_scale<q>(av, bg[nj][q], accg[nj], sg[nj]);
-                accu[nj] = mfma_packed_scale<q>(av, bu[nj][q], accu[nj], su[nj]);
-            }
-        });
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                red[w][nj][0][i][lane] = has_k ? accg[nj][i] : 0.0f;
-                red[w][nj][1][i][lane] = has_k ? accu[nj][i] : 0.0f;
-            }
-        }
-        if (w == 0 && g == 0) tok_scale[r] = s_row;
-        if (tile + 1 < ntiles) load_tile(tok[tile + 1 < kChunkTiles ? tile + 1 : 0]);   // in flight meanwhile
-        __syncthreads();
-        // thread (ii, l) finalises C[4 (l >> 4) + ii][l & 15] of each n-tile
-        const int l = threadIdx.x & 63, ii = threadIdx.x >> 6;
-        const int trow = 4 * (l >> 4) + ii;
-        const int row = tile * 16 + trow;
-        const float sc = tok_scale[trow];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            float gs = red[0][nj][0][ii][l], us = red[0][nj][1][ii][l];
-#pragma unroll
-            for (int v = 1; v < G::KSPLIT; ++v) {
-                gs += red[v][nj][0][ii][l];
-                us += red[v][nj][1][ii][l];
-            }
-            if (row < n) {
-                const float gv = gs * sc, uv = us * sc;
-                a.h[(size_t)(off + row) * I + j0 + 16 * nj + (l & 15)] = gv / (1.0f + expf(-gv)) * uv;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Down: workgroup (chunk, nq) owns output rows [kDnRows nq, kDnRows (nq + 1))
-// of the chunk's expert; wave w holds the down weights of its NJ 16-row
-// n-tiles (all of K = I) in registers, the block scales come through LDS, and
-// the chunk's token tiles run through them, every activation load of a tile
-// issued before its MFMAs (one activation operand feeds NJ MFMAs) and the
-// next tile's loads in flight while the current tile is stored.
-// y[pos, n] = s2 * acc (the router weight is applied by the combine).
-// ---------------------------------------------------------------------------
-constexpr int kDnNJ = 2;
-constexpr int kDnRows = 4 * 16 * kDnNJ;                 // 4 waves x NJ n-tiles x 16 rows
-
-template <int H, int I, bool BY_PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void chunk_down_kernel(
-    ChunkDownArgs a)
-{
-    static_assert(H % kDnRows == 0 && I % 32 == 0, "chunk down row blocking");
-    constexpr int KS = (I + 127) / 128, NJ = kDnNJ, SROW = I / 32;
-    constexpr int SBYTES = kDnRows * SROW;
-    __shared__ alignas(16) uint8_t sc_lds[(SBYTES + 15) / 16 * 16];
-    const int nq = blockIdx.x % (H / kDnRows);
-    const int4 rec = a.chunks.rec[blockIdx.x / (H / kDnRows)];
-    const int e = rec.x, off = rec.y, n = rec.z;
-    if (n == 0) return;                                 // whole workgroup: past the last chunk
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const int n0 = nq * kDnRows;
-    const uint8_t* w2e = e == kSharedExpert ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
-    const uint8_t* sw2e = e == kSharedExpert ? a.sh.s2 : a.sw2 + (size_t)e * H * SROW;
-    i32x8 b[NJ][KS];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-        const uint8_t* wrow = w2e + (size_t)(n0 + (w * NJ + nj) * 16 + r) * (I / 2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int kb = ks * 128 + 32 * g;             // first K of this lane's block
-            if constexpr (I % 128 == 0) {
-                b[nj][ks] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wrow + kb / 2)));
-            } else {                                      // K padded with zero codes
-                const bool in = kb < I;
-                b[nj][ks] = in ? fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wrow + (in ? kb / 2 : 0))))
-                               : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-    }
-    if constexpr (SBYTES % 16 == 0) {
-        copy_to_lds(sc_lds, sw2e + (size_t)n0 * SROW, SBYTES);
-    } else {
-        for (int i = threadIdx.x; i < SBYTES; i += 256) sc_lds[i] = sw2e[(size_t)n0 * SROW + i];
-    }
-    u32x4 alo[KS], ahi[KS];
-    float es[4];                                          // s2 of the rows this lane stores
-    auto load_tile = [&](int base) {
-        const int row = base + r;
-        const int pos = off + (row < n ? row : n - 1);
-        const int arow = BY_PAIR ? a.cp.pair_src[pos] : pos;
-        const uint8_t* q = a.q2 + (size_t)arow * I + 16 * g;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (I % 128 == 0) {
-                alo[ks] = *reinterpret_cast<const u32x4*>(q + ks * 128);
-                ahi[ks] = *reinterpret_cast<const u32x4*>(q + ks * 128 + 64);
-            } else {
-                const bool lo_in = ks * 128 + 16 * g + 16 <= I, hi_in = ks * 128 + 64 + 16 * g + 16 <= I;
-                alo[ks] = lo_in ? *reinterpret_cast<const u32x4*>(q + (lo_in ? ks * 128 : 0)) : u32x4{0u, 0u, 0u, 0u};
-                ahi[ks] = hi_in ? *reinterpret_cast<const u32x4*>(q + (hi_in ? ks * 128 + 64 : 0))
-                                : u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row2 = base + 4 * g + i;
-            const int pos2 = off + (row2 < n ? row2 : n - 1);
-            es[i] = a.s2[BY_PAIR ? a.cp.pair_src[pos2] : pos2];
-        }
-    };
-    load_tile(0);
-    __syncthreads();                                      // block scales in LDS
-    constexpr int NP = (KS + 3) / 4;                    // packed scale registers per n-tile
-    int sc[NJ][NP];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-#pragma unroll
-        for (int u = 0; u < NP; ++u) sc[nj][u] = 0;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int kb = ks * 128 + 32 * g;
-            const int code = (kb < I) ? sc_lds[((w * NJ + nj) * 16 + r) * SROW + (kb < I ? kb / 32 : 0)] : 127;
-            sc[nj][ks / 4] |= code << (8 * (ks % 4));
-        }
-    }
-    for (int base = 0; base < n; base += 16) {
-        f32x4 acc[NJ];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) acc[nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        static_for<KS>([&](auto kc) {
-            constexpr int ks = decltype(kc)::value;
-            const i32x8 av = fp8_operand(alo[ks], ahi[ks]);
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj) acc[nj] = mfma_packed_scale<ks>(av, b[nj][ks], acc[nj], sc[nj]);
-        });
-        float esc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) esc[i] = es[i];
-        if (base + 16 < n) load_tile(base + 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row2 = base + 4 * g + i;
-            if (row2 < n) {
-                float* yr = a.y + (size_t)(off + row2) * H + n0 + w * NJ * 16 + r;
-#pragma unroll
-                for (int nj = 0; nj < NJ; ++nj) yr[16 * nj] = acc[nj][i] * esc[i];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Combine: out[t, :] = sum_{j < K} w[t, j] * y[pos_of[t K + j], :], added in
-// j order, then (with a shared expert) + y[pos_of[M K + t], :].
-// ---------------------------------------------------------------------------
-template <int H>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
-{
-    constexpr int Q = H / 4;
-    const int total = a.M * Q;
-    for (int idx = blockIdx.x * 256 + threadIdx.x; idx < total; idx += gridDim.x * 256) {
-        const int t = idx / Q, c = (idx - t * Q) * 4;
-        float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int j = 0; j < a.K; ++j) {
-            const int pos = a.pos_of[t * a.K + j];
-            const float wj = a.w[t * a.K + j];
-            const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)pos * H + c);
-            s.x += wj * v.x; s.y += wj * v.y; s.z += wj * v.z; s.w += wj * v.w;
-        }
-        if (a.shared != 0) {
-            const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)a.pos_of[a.M * a.K + t] * H + c);
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-        }
-        *reinterpret_cast<float4*>(a.out + (size_t)t * H + c) = s;
-    }
-}
-
-// dst row p = src row pos_of[p] (rows of `words` 32-bit words): turns
-// sorted-order intermediates into pair order for the caller's taps.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
-                                                          const int32_t* __restrict__ pos_of, int P, int words)
-{
-    const int64_t total = (int64_t)P * words;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int p = (int)(idx / words), w = (int)(idx - (int64_t)p * words);
-        dst[idx] = src[(int64_t)pos_of[p] * words + w];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Launchers.
-// ---------------------------------------------------------------------------
 template <typename F, typename... Args>
-static void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, const LaunchEvents& ev, Args... args)
+static hipError_t launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, const LaunchEvents& ev,
+                         Args... args)
 {
     if (ev.start != nullptr || ev.stop != nullptr)
         hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
     else
         hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
 }
 
+// The chunk path has kernels for (H, I) (compiled in, or loaded at run time)
+// and E splits into 16-expert router tiles.
 bool chunk_shape_supported(int H, int I, int E)
 {
-    return ((H == 256 && I == 64) || (H == 2560 && I == 768)) && E % 16 == 0;
+    return chunk_shape_ok(H, I) && E % 16 == 0 && find_kernel(key_chunk_gate_up(H, I)).ok();
 }
 
 hipError_t launch_chunk_router(int H, const ChunkRouterArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
+    const Kern k = find_kernel(key_chunk_router(H));
+    if (!k.ok()) return hipErrorInvalidDeviceFunction;
     const dim3 grid((unsigned)(((a.M + 15) / 16) * (a.E / 16)));
-    const dim3 block(kRouterWaves * kWave);
-    if (H == 256) launch(chunk_router_kernel<256>, grid, block, 0, s, ev, a);
-    else if (H == 2560) launch(chunk_router_kernel<2560>, grid, block, 0, s, ev, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    return launch_kern(k, grid, dim3(kRouterWaves * kWave), 0, s, ev, a);
 }
 
 hipError_t launch_chunk_topk(const ChunkTopkArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    launch(chunk_topk_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, ev, a);
-    return hipGetLastError();
+    return launch(chunk_topk_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_sort_pairs(const SortArgs& a, hipStream_t s, const LaunchEvents& ev)
@@ -657,44 +73,30 @@ hipError_t launch_sort_pairs(const SortArgs& a, hipStream_t s, const LaunchEvent
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
     }
-    launch(sort_pairs_kernel, dim3(1), dim3(kSortThreads), (uint32_t)lds, s, ev, a);
-    return hipGetLastError();
+    return launch(sort_pairs_kernel, dim3(1), dim3(kSortThreads), (uint32_t)lds, s, ev, a);
 }
 
 hipError_t launch_chunk_gate_up(int H, int I, int C, const ChunkGateUpArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    const dim3 grid((unsigned)(C * (I / kGuRows)));
-    if (H == 256 && I == 64) launch(chunk_gate_up_kernel<256, 64>, grid, dim3(256), 0, s, ev, a);
-    else if (H == 2560 && I == 768) launch(chunk_gate_up_kernel<2560, 768>, grid, dim3(256), 0, s, ev, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    const Kern k = find_kernel(key_chunk_gate_up(H, I));
+    if (!k.ok()) return hipErrorInvalidDeviceFunction;
+    return launch_kern(k, dim3((unsigned)(C * (I / kGuRows))), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_chunk_down(int H, int I, int C, const ChunkDownArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    const dim3 grid((unsigned)(C * (H / kDnRows)));
-    const bool bp = a.by_pair != 0;
-    if (H == 256 && I == 64) {
-        if (bp) launch(chunk_down_kernel<256, 64, true>, grid, dim3(256), 0, s, ev, a);
-        else launch(chunk_down_kernel<256, 64, false>, grid, dim3(256), 0, s, ev, a);
-    } else if (H == 2560 && I == 768) {
-        if (bp) launch(chunk_down_kernel<2560, 768, true>, grid, dim3(256), 0, s, ev, a);
-        else launch(chunk_down_kernel<2560, 768, false>, grid, dim3(256), 0, s, ev, a);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const Kern k = find_kernel(key_chunk_down(H, I, a.by_pair != 0));
+    if (!k.ok()) return hipErrorInvalidDeviceFunction;
+    return launch_kern(k, dim3((unsigned)(C * (H / kDnRows))), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_combine(int H, const CombineArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
+    const Kern k = find_kernel(key_combine(H));
+    if (!k.ok()) return hipErrorInvalidDeviceFunction;
     const int total = a.M * (H / 4);
     const int blocks = (total + 255) / 256;
-    const dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));
-    if (H == 256) launch(combine_kernel<256>, grid, dim3(256), 0, s, ev, a);
-    else if (H == 2560) launch(combine_kernel<2560>, grid, dim3(256), 0, s, ev, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    return launch_kern(k, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of, int P, int row_bytes, hipStream_t s)
@@ -709,18 +111,16 @@ hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of,
     return hipGetLastError();
 }
 
-const char* chunk_kernel_names(int H, int I)
+void chunk_kernel_names(int H, int I, char* buf, size_t n)
 {
-    if (H == 2560 && I == 768)
-        return "chunk_router_kernel<H=2560> (bf16 MFMA 16x16x32) -> quant_kernel<2560> -> chunk_topk_kernel -> "
-               "sort_pairs_kernel (1 workgroup: token bitmasks in LDS) -> chunk_gate_up_kernel<2560,768> (scaled "
-               "FP8xFP4 MFMA 16x16x128, 24 workgroups per 64-token chunk, K split over 4 waves) -> "
-               "requant_kernel<768> -> chunk_down_kernel<2560,768> (scaled FP8xFP4 MFMA, 20 workgroups per chunk) "
-               "-> combine_kernel<2560>";
-    if (H == 256 && I == 64)
-        return "chunk_router_kernel<H=256> -> quant_kernel<256> -> chunk_topk_kernel -> sort_pairs_kernel -> "
-               "chunk_gate_up_kernel<256,64> -> requant_kernel<64> -> chunk_down_kernel<256,64> -> combine_kernel<256>";
-    return "unsupported";
+    const Kern k = find_kernel(key_chunk_gate_up(H, I));
+    snprintf(buf, n,
+             "chunk_router_kernel<H=%d> (bf16 MFMA 16x16x32) -> quant_kernel<%d> -> chunk_topk_kernel -> "
+             "sort_pairs_kernel (1 workgroup: token bitmasks in LDS) -> chunk_gate_up_kernel<%d,%d> (scaled FP8xFP4 "
+             "MFMA 16x16x128, %d workgroups per 64-token chunk, K split over %d waves) -> requant_kernel<%d> -> "
+             "chunk_down_kernel<%d,%d> (scaled FP8xFP4 MFMA, %d workgroups per chunk) -> combine_kernel<%d>%s",
+             H, H, H, I, I / kGuRows, chunk_k_split(H), I, H, I, H / kDnRows, H,
+             k.jit != nullptr ? " [compiled at run time]" : "");
 }
 
 }  // namespace moe

@@ -1,174 +1,21 @@
-// moe_internal.hpp -- kernel argument blocks, workspace layout and launcher
-// declarations shared by the kernels (moe_kernels.hip) and the C ABI
-// (moe_api.hip).  Not installed; the public interface is include/moe_decode.h.
+// moe_internal.hpp -- host side of the library: workspace layout, launch
+// events and the launcher declarations shared by the kernels' launch code and
+// the C ABI (moe_api.hip).  Not installed; the public interface is
+// include/moe_decode.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "moe_types.hpp"
+
 namespace moe {
 
-// Largest token count of the GEMV path, and largest K / E it supports.
-constexpr int kMaxGemvTokens = 8;
-constexpr int kMaxTopK = 8;
-constexpr int kMaxExperts = 512;
-constexpr int kMaxPairs = kMaxGemvTokens * kMaxTopK;
-// With a shared expert every token adds one pair (row P + t of the
-// intermediates) in one more slot, whose expert id is kSharedExpert.
-constexpr int kMaxPairsExt = kMaxPairs + kMaxGemvTokens;
-constexpr int kSharedExpert = -1;
-// Largest token count of the chunk path (M > kMaxGemvTokens): its M*K pairs
-// are sorted by expert in one workgroup's LDS.
-constexpr int kMaxChunkTokens = 2048;
-constexpr int kMaxChunkPairs = kMaxChunkTokens * kMaxTopK;
-
-// The shared expert's weights (one expert of the routed layout), or all null.
-struct SharedWeights {
-    const uint8_t* w13;    // [2I,H/2]
-    const uint8_t* s13;    // [2I,H/32]
-    const uint8_t* w2;     // [H,I/2]
-    const uint8_t* s2;     // [H,I/32]
-};
-
-// Token -> expert compaction as published in the workspace.
-struct Compaction {
-    int32_t* n_act;        // [1]
-    int32_t* act_experts;  // [S] ascending expert ids
-    int32_t* offsets;      // [S+1]
-    int32_t* pair_token;   // [M*K]
-    int32_t* pair_src;     // [M*K] original pair index t*K+j
-};
-
-struct RouterArgs {
-    const uint16_t* x;     // [M,H] bf16
-    const uint16_t* wr;    // [E,H] bf16
-    int M, E;
-    float* logits;         // [M,E]
-    uint8_t* act_q;        // [M,H] or nullptr (no quantisation)
-    float* act_s;          // [M]
-};
-
-// Routing source of a prologue: logits (top-K computed in the workgroup) or
-// caller-given ids.
-struct RouteSrc {
-    int M, E, K;
-    const float* logits;   // [M,E] or nullptr
-    const int32_t* ids;    // [M,K] used when logits is nullptr
-    int shared;            // 1: append the shared expert's slot
-};
-
-struct TopkArgs {
-    RouteSrc src;
-    int32_t* ids_out;      // [M,K]
-    float* w_out;          // [M,K] (only with logits)
-    Compaction cp;
-};
-
-struct GateUpArgs {
-    RouteSrc src;          // logits (top-K in every workgroup) or caller ids
-    int32_t* ids_out;      // [M,K] published by workgroup 0; may be nullptr
-    float* w_out;          // [M,K]; may be nullptr
-    Compaction cp;         // published by workgroup 0
-    const uint8_t* w13;    // [E,2I,H/2]
-    const uint8_t* s13;    // [E,2I,H/32]
-    const uint8_t* act_q;  // [M,H]
-    const float* act_s;    // [M]
-    float* h;              // [M*K (+M),I]
-    SharedWeights sh;      // read when the compaction holds the shared slot
-};
-
-struct DownArgs {
-    int E, M, K;
-    const uint8_t* w2;     // [E,H,I/2]
-    const uint8_t* sw2;    // [E,H,I/32]
-    const float* h;        // [M*K,I] fp32, requantised in the kernel; or nullptr
-    const uint8_t* q2;     // [M*K,I] E4M3 intermediate, used when h is nullptr
-    const float* s2;       // [M*K]
-    uint8_t* q2_out;       // optional: the requantised codes (workgroup 0 writes them)
-    float* s2_out;         // optional: their scales
-    const float* topk_w;   // [M*K]
-    Compaction cp;         // read
-    float* out;            // [M,H]
-    SharedWeights sh;      // non-null w2: the compaction's last slot is the shared expert (weight 1)
-};
-
-struct RequantArgs {
-    const float* h;        // [P,I]
-    int P;
-    uint8_t* q2;           // [P,I]
-    float* s2;             // [P]
-};
-
-// Chunk path (M > kMaxGemvTokens): grouped contractions over the expert-sorted
-// pairs.  "Sorted position" pos indexes the pairs in (expert, pair index)
-// order, as in Compaction; pos_of[p] is the sorted position of pair p.
-struct ChunkRouterArgs {
-    const uint16_t* x;     // [M,H] bf16
-    const uint16_t* wr;    // [E,H] bf16
-    int M, E;
-    float* logits;         // [M,E]
-};
-
-struct ChunkTopkArgs {
-    const float* logits;   // [M,E]
-    int M, E, K;
-    int32_t* ids;          // [M,K]
-    float* w;              // [M,K]
-};
-
-// Work list of the grouped kernels: the sorted rows of each active expert
-// cut into chunks of at most kChunkRows rows, larger chunks first.
-constexpr int kChunkRows = 64;
-
-struct ChunkList {
-    int32_t* n_chunks;     // [1]
-    int4* rec;             // [C] {expert, first sorted position, rows, 0}; rows = 0 past the last chunk
-    int C;                 // entries of rec (chunk_bound)
-};
-
-inline int chunk_bound(int S, int P) { return S + (P + kChunkRows - 1) / kChunkRows; }
-
-struct SortArgs {
-    const int32_t* ids;    // [M,K]; out-of-range ids are clamped into [0, E)
-    int M, K, E;
-    Compaction cp;         // written
-    int32_t* pos_of;       // [M*K (+M)]
-    ChunkList chunks;      // written
-    int shared;            // 1: the shared expert's M rows follow as one more slot
-};
-
-struct ChunkGateUpArgs {
-    Compaction cp;         // read
-    ChunkList chunks;      // read
-    const uint8_t* w13;    // [E,2I,H/2]
-    const uint8_t* s13;    // [E,2I,H/32]
-    const uint8_t* act_q;  // [M,H]
-    const float* act_s;    // [M]
-    float* h;              // [M*K (+M),I] in sorted order
-    SharedWeights sh;
-};
-
-struct ChunkDownArgs {
-    Compaction cp;         // read
-    ChunkList chunks;      // read
-    const uint8_t* w2;     // [E,H,I/2]
-    const uint8_t* sw2;    // [E,H,I/32]
-    const uint8_t* q2;     // [M*K,I] E4M3 intermediate
-    const float* s2;       // [M*K]
-    int by_pair;           // 0: q2/s2 rows in sorted order; 1: in pair order
-    float* y;              // [M*K (+M),H] expert outputs (s2 applied) in sorted order
-    SharedWeights sh;
-};
-
-struct CombineArgs {
-    const float* y;        // [M*K,H] sorted order
-    const int32_t* pos_of; // [M*K]
-    const float* w;        // [M*K] router weights in pair order
-    int M, K;
-    float* out;            // [M,H]
-    int shared;            // 1: add the shared expert's row y[pos_of[M*K + t]] (weight 1)
-};
+// Dynamic LDS a kernel may take on gfx950 (160 KiB per compute unit).
+constexpr size_t kMaxDynamicLds = 160 * 1024;
 
 // Workspace carving.  No state is carried between calls: every call writes
 // what it later reads.  pos_of and y exist only for the chunk path.
@@ -219,8 +66,10 @@ struct LaunchEvents {
     hipEvent_t stop = nullptr;
 };
 
-// Launchers (moe_kernels.hip).  Each returns the hipError_t of its launch.
-// mt is the token bound the kernels are instantiated for (1, 2, 4 or 8).
+// Launchers (moe_kernels.hip).  Each returns the hipError_t of its launch
+// (hipErrorInvalidDeviceFunction when the shape has no kernel: neither
+// compiled in nor loaded at run time).  mt is the token bound the kernels are
+// instantiated for (1, 2, 4 or 8).
 bool gemv_shape_supported(int H, int I);
 hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_quant(int H, const uint16_t* x, int M, uint8_t* q, float* sc, hipStream_t s);
@@ -231,7 +80,7 @@ hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, c
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
-const char* kernel_names(int H, int I, int mt);
+void kernel_names(int H, int I, char* buf, size_t n);
 
 // Chunk-path launchers (moe_chunk.hip).
 bool chunk_shape_supported(int H, int I, int E);
@@ -244,12 +93,30 @@ hipError_t launch_chunk_gate_up(int H, int I, int C, const ChunkGateUpArgs& a, h
 hipError_t launch_chunk_down(int H, int I, int C, const ChunkDownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_combine(int H, const CombineArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* pos_of, int P, int row_bytes, hipStream_t s);
-const char* chunk_kernel_names(int H, int I);
+void chunk_kernel_names(int H, int I, char* buf, size_t n);
 
 // FP8 LM head (lm_head.hip).  mt is the token bound (1, 2, 4 or 8).
 bool lm_head_shape_supported(int H);
 hipError_t launch_lm_head_quant(const uint16_t* w, int V, int H, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_lm_head_gemv(int H, int mt, const uint16_t* x, int M, const uint8_t* q, const float* scale, int V,
                                float* logits, hipStream_t s);
+
+// Run-time compilation of the shape-templated kernels (jit.hip).
+enum class JitStatus { Ok, BadShape, BadArch, CacheIo, Compile, Load };
+struct JitReport {
+    bool from_cache = false;   // the code object came from the cache file
+    bool chunk = false;        // the module holds the chunk-path kernels
+    bool lm_head = false;      // ... and the LM-head GEMV for this H
+    int kernels = 0;
+    double seconds = 0.0;
+    char file[1024] = "";
+};
+// Compile (or find in the cache) the kernels of (H, I) for `arch`; no device needed.
+JitStatus jit_build(int H, int I, const char* arch, const char* cache_dir, JitReport* rep, std::string* err);
+// The same for the current device, then load them on it.  prefer: use them
+// even where a compiled-in kernel exists.
+JitStatus jit_load(int H, int I, const char* cache_dir, bool prefer, JitReport* rep, std::string* err);
+// Unload (H, I) from the current device; returns the number of modules removed.
+int jit_unload(int H, int I);
 
 }  // namespace moe

@@ -1,0 +1,228 @@
+// moe_types.hpp -- constants, kernel argument blocks and shape geometry shared
+// by the device code (compiled ahead of time by hipcc and at run time by
+// hipRTC) and the host launchers.  Device-compilable under hipRTC: no host
+// runtime headers.
+#pragma once
+
+#ifndef __HIPCC_RTC__
+#include <hip/hip_runtime.h>
+#endif
+#include <stdint.h>
+
+namespace moe {
+
+
+// Largest token count of the GEMV path, and largest K / E it supports.
+constexpr int kMaxGemvTokens = 8;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxPairs = kMaxGemvTokens * kMaxTopK;
+// With a shared expert every token adds one pair (row P + t of the
+// intermediates) in one more slot, whose expert id is kSharedExpert.
+constexpr int kMaxPairsExt = kMaxPairs + kMaxGemvTokens;
+constexpr int kSharedExpert = -1;
+// Largest token count of the chunk path (M > kMaxGemvTokens): its M*K pairs
+// are sorted by expert in one workgroup's LDS.
+constexpr int kMaxChunkTokens = 2048;
+constexpr int kMaxChunkPairs = kMaxChunkTokens * kMaxTopK;
+
+// The shared expert's weights (one expert of the routed layout), or all null.
+struct SharedWeights {
+    const uint8_t* w13;    // [2I,H/2]
+    const uint8_t* s13;    // [2I,H/32]
+    const uint8_t* w2;     // [H,I/2]
+    const uint8_t* s2;     // [H,I/32]
+};
+
+// Token -> expert compaction as published in the workspace.
+struct Compaction {
+    int32_t* n_act;        // [1]
+    int32_t* act_experts;  // [S] ascending expert ids
+    int32_t* offsets;      // [S+1]
+    int32_t* pair_token;   // [M*K]
+    int32_t* pair_src;     // [M*K] original pair index t*K+j
+};
+
+struct RouterArgs {
+    const uint16_t* x;     // [M,H] bf16
+    const uint16_t* wr;    // [E,H] bf16
+    int M, E;
+    float* logits;         // [M,E]
+    uint8_t* act_q;        // [M,H] or nullptr (no quantisation)
+    float* act_s;          // [M]
+};
+
+// Routing source of a prologue: logits (top-K computed in the workgroup) or
+// caller-given ids.
+struct RouteSrc {
+    int M, E, K;
+    const float* logits;   // [M,E] or nullptr
+    const int32_t* ids;    // [M,K] used when logits is nullptr
+    int shared;            // 1: append the shared expert's slot
+};
+
+struct TopkArgs {
+    RouteSrc src;
+    int32_t* ids_out;      // [M,K]
+    float* w_out;          // [M,K] (only with logits)
+    Compaction cp;
+};
+
+struct GateUpArgs {
+    RouteSrc src;          // logits (top-K in every workgroup) or caller ids
+    int32_t* ids_out;      // [M,K] published by workgroup 0; may be nullptr
+    float* w_out;          // [M,K]; may be nullptr
+    Compaction cp;         // published by workgroup 0
+    const uint8_t* w13;    // [E,2I,H/2]
+    const uint8_t* s13;    // [E,2I,H/32]
+    const uint8_t* act_q;  // [M,H]
+    const float* act_s;    // [M]
+    float* h;              // [M*K (+M),I]
+    SharedWeights sh;      // read when the compaction holds the shared slot
+};
+
+struct DownArgs {
+    int E, M, K;
+    const uint8_t* w2;     // [E,H,I/2]
+    const uint8_t* sw2;    // [E,H,I/32]
+    const float* h;        // [M*K,I] fp32, requantised in the kernel; or nullptr
+    const uint8_t* q2;     // [M*K,I] E4M3 intermediate, used when h is nullptr
+    const float* s2;       // [M*K]
+    uint8_t* q2_out;       // optional: the requantised codes (workgroup 0 writes them)
+    float* s2_out;         // optional: their scales
+    const float* topk_w;   // [M*K]
+    Compaction cp;         // read
+    float* out;            // [M,H]
+    SharedWeights sh;      // non-null w2: the compaction's last slot is the shared expert (weight 1)
+};
+
+struct RequantArgs {
+    const float* h;        // [P,I]
+    int P;
+    uint8_t* q2;           // [P,I]
+    float* s2;             // [P]
+};
+
+// Chunk path (M > kMaxGemvTokens): grouped contractions over the expert-sorted
+// pairs.  "Sorted position" pos indexes the pairs in (expert, pair index)
+// order, as in Compaction; pos_of[p] is the sorted position of pair p.
+struct ChunkRouterArgs {
+    const uint16_t* x;     // [M,H] bf16
+    const uint16_t* wr;    // [E,H] bf16
+    int M, E;
+    float* logits;         // [M,E]
+};
+
+struct ChunkTopkArgs {
+    const float* logits;   // [M,E]
+    int M, E, K;
+    int32_t* ids;          // [M,K]
+    float* w;              // [M,K]
+};
+
+// Work list of the grouped kernels: the sorted rows of each active expert
+// cut into chunks of at most kChunkRows rows, larger chunks first.
+constexpr int kChunkRows = 64;
+
+struct ChunkList {
+    int32_t* n_chunks;     // [1]
+    int4* rec;             // [C] {expert, first sorted position, rows, 0}; rows = 0 past the last chunk
+    int C;                 // entries of rec (chunk_bound)
+};
+
+__host__ __device__ constexpr int chunk_bound(int S, int P) { return S + (P + kChunkRows - 1) / kChunkRows; }
+
+struct SortArgs {
+    const int32_t* ids;    // [M,K]; out-of-range ids are clamped into [0, E)
+    int M, K, E;
+    Compaction cp;         // written
+    int32_t* pos_of;       // [M*K (+M)]
+    ChunkList chunks;      // written
+    int shared;            // 1: the shared expert's M rows follow as one more slot
+};
+
+struct ChunkGateUpArgs {
+    Compaction cp;         // read
+    ChunkList chunks;      // read
+    const uint8_t* w13;    // [E,2I,H/2]
+    const uint8_t* s13;    // [E,2I,H/32]
+    const uint8_t* act_q;  // [M,H]
+    const float* act_s;    // [M]
+    float* h;              // [M*K (+M),I] in sorted order
+    SharedWeights sh;
+};
+
+struct ChunkDownArgs {
+    Compaction cp;         // read
+    ChunkList chunks;      // read
+    const uint8_t* w2;     // [E,H,I/2]
+    const uint8_t* sw2;    // [E,H,I/32]
+    const uint8_t* q2;     // [M*K,I] E4M3 intermediate
+    const float* s2;       // [M*K]
+    int by_pair;           // 0: q2/s2 rows in sorted order; 1: in pair order
+    float* y;              // [M*K (+M),H] expert outputs (s2 applied) in sorted order
+    SharedWeights sh;
+};
+
+struct CombineArgs {
+    const float* y;        // [M*K,H] sorted order
+    const int32_t* pos_of; // [M*K]
+    const float* w;        // [M*K] router weights in pair order
+    int M, K;
+    float* out;            // [M,H]
+    int shared;            // 1: add the shared expert's row y[pos_of[M*K + t]] (weight 1)
+};
+
+// ---------------------------------------------------------------------------
+// Shape geometry, as constexpr functions so that the kernel templates and the
+// host launchers (which also launch kernels compiled at run time for shapes
+// known only then) compute the same blocking.
+// ---------------------------------------------------------------------------
+constexpr int kWaveSize = 64;
+
+// gate/up GEMV: H/32 chunks of 16 code bytes per row, LPR lanes per row.
+__host__ __device__ constexpr int gate_up_lanes_per_row(int H)
+{
+    return ((H / 32) % 16 == 0) ? 16 : ((H / 32) % 8 == 0) ? 8 : ((H / 32) % 4 == 0) ? 4 : ((H / 32) % 2 == 0) ? 2 : 1;
+}
+__host__ __device__ constexpr int gate_up_rows_per_block(int H) { return (kWaveSize / gate_up_lanes_per_row(H)) * 4; }
+
+// down GEMV: I/32 chunks per row, LPR lanes per row, one row per LPR lanes.
+__host__ __device__ constexpr int down_lanes_per_row(int I)
+{
+    return ((I / 32) % 8 == 0) ? 8 : ((I / 32) % 4 == 0) ? 4 : ((I / 32) % 2 == 0) ? 2 : 1;
+}
+__host__ __device__ constexpr int down_rows_per_block(int I) { return kWaveSize / down_lanes_per_row(I); }
+
+// The decode (GEMV) path's kernels exist for (H, I) when these hold (the
+// kernels' own static checks repeat them).
+__host__ __device__ constexpr bool gemv_shape_ok(int H, int I)
+{
+    return H >= 256 && H <= 8192 && H % 32 == 0 && I >= 64 && I <= 4096 && I % kWaveSize == 0 &&
+           I % gate_up_rows_per_block(H) == 0 && H % down_rows_per_block(I) == 0;
+}
+
+// Chunk path blocking: 16-row MFMA tiles, 64-row chunks, 32 gate/up rows and
+// 128 down rows per workgroup, router K slices of H/8.
+constexpr int kChunkTiles = kChunkRows / 16;
+constexpr int kGuNJ = 2;                                // 16-row n-tiles per wave and matrix
+constexpr int kGuRows = 16 * kGuNJ;
+constexpr int kDnNJ = 2;
+constexpr int kDnRows = 4 * 16 * kDnNJ;                 // 4 waves x NJ n-tiles x 16 rows
+constexpr int kRouterWaves = 8;
+
+__host__ __device__ constexpr int chunk_k_steps(int H) { return H / 128; }
+__host__ __device__ constexpr int chunk_k_split(int H) { return chunk_k_steps(H) >= 4 ? 4 : chunk_k_steps(H); }
+
+__host__ __device__ constexpr bool chunk_shape_ok(int H, int I)
+{
+    return gemv_shape_ok(H, I) && H % (kRouterWaves * 32) == 0 && H % 128 == 0 &&
+           chunk_k_steps(H) % chunk_k_split(H) == 0 && I % kGuRows == 0 && (kGuRows * (H / 32)) % 16 == 0 &&
+           H % kDnRows == 0 && I % 32 == 0;
+}
+
+// FP8 LM-head GEMV: 16 lanes per row, each taking 16-code chunks; the
+// activations of up to 8 tokens stay in LDS (16 H bytes).
+__host__ __device__ constexpr bool lm_head_shape_ok(int H) { return H >= 256 && H <= 4096 && H % 256 == 0; }
+
+}  // namespace moe

@@ -11,7 +11,7 @@
 #pragma once
 
 #include "device_common.hpp"
-#include "moe_internal.hpp"
+#include "moe_types.hpp"
 
 namespace moe {
 
