@@ -489,19 +489,12 @@ def chunk_bench(args, moe, synth, stack, shp, stream) -> dict:
 # HBM traffic of the gate/up kernel comes from hardware counters taken with
 # rocprofv3 (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
 # and is only reported while the kernel source is the one it was taken on.
-KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
-                  "mxfp4_weight_streaming_amd/csrc/device_common.hpp",
-                  "mxfp4_weight_streaming_amd/csrc/topk_wave.hpp"]
 TRAFFIC_FILE = "profiles/gate_up_hbm_traffic.txt"
 
 
 def kernel_source_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    from mxfp4_weight_streaming_amd.profiling import kernel_source_hash as h
+    return h()
 
 
 def measured_traffic():

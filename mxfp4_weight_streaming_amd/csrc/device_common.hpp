@@ -191,6 +191,18 @@ __device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane)
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// The row results of a 32-bit reduction are combined across rows on DPP as
+// well: row_bcast:15 gives rows 1 and 3 the combination with the row before,
+// row_bcast:31 gives rows 2 and 3 the combination with rows 0-1, so lane 63
+// ends with the whole wave's result (one readlane instead of four).
+enum : int { kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143 };
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32_rows(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+
 // Wave-wide maximum of an unsigned 32-bit value (uniform result).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
@@ -198,9 +210,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     v = max(v, dpp_u32<kDppXor2>(v));
     v = max(v, dpp_u32<kDppHalfMirror>(v));
     v = max(v, dpp_u32<kDppMirror>(v));
-    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-    return max(a, b);
+    v = max(v, dpp_u32_rows<kDppRowBcast15, 0xA>(v));
+    v = max(v, dpp_u32_rows<kDppRowBcast31, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Wave-wide minimum of an unsigned 32-bit value (uniform result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = min(v, dpp_u32<kDppXor1>(v));
+    v = min(v, dpp_u32<kDppXor2>(v));
+    v = min(v, dpp_u32<kDppHalfMirror>(v));
+    v = min(v, dpp_u32<kDppMirror>(v));
+    v = min(v, dpp_u32_rows<kDppRowBcast15, 0xA>(v));
+    v = min(v, dpp_u32_rows<kDppRowBcast31, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Wave-wide maximum of a 64-bit key; the result is uniform across the wave.

@@ -331,6 +331,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, BPE = G::kBlocksPerExpert;
     __shared__ RouteLds rl;
     __shared__ u32x4 act[MT * 4 * CH];          // [token][q][chunk] of 8 halves
+    __shared__ float act_sl[MT];                // per-token activation scales
 
     const int M = a.src.M;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     u32x2 stg[NST];
 #pragma unroll
     for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
+    const float s_tok = a.act_s[min((int)threadIdx.x, M - 1)];
     // 1. routing, derived independently by every workgroup (the staging loads
     //    above are in flight meanwhile); workgroup 0 publishes it for the down
     //    kernel (and the caller)
@@ -356,6 +358,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
         }
     }
+    if ((int)threadIdx.x < M) act_sl[threadIdx.x] = s_tok;
     __syncthreads();
     const int n_items = rl.n_act * BPE;
 
@@ -423,28 +426,53 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             if (t < nt) {
                 accg[t] = group_sum<LPR>(accg[t]);
                 accu[t] = group_sum<LPR>(accu[t]);
-                const float sc = a.act_s[rl.pair_token[p0 + t]];
+                const float sc = act_sl[rl.pair_token[p0 + t]];
                 const float g = accg[t] * sc, u = accu[t] * sc;
                 if (li == 0) a.h[(size_t)rl.pair_src[p0 + t] * I + r] = g / (1.0f + expf(-g)) * u;
             }
         }
     };
 
-    int item = blockIdx.x;
-    if (item >= n_items) return;
-    Stage s0, s1;
-    issue(item, s0);
-    for (;;) {
-        const int next = item + gridDim.x;
-        if (next < n_items) issue(next, s1);
-        compute(item, s0);
-        if (next >= n_items) break;
-        item = next;
-        const int after = item + gridDim.x;
-        if (after < n_items) issue(after, s0);
-        compute(item, s1);
-        if (after >= n_items) break;
-        item = after;
+    // Items blockIdx.x, blockIdx.x + grid, ...: the next item's loads are
+    // issued before the current one is computed.
+    constexpr int IPW = ((MT * kMaxTopK + 1) * BPE + 511) / 512;   // most items per workgroup
+    if ((int)blockIdx.x >= n_items) return;
+    Stage st[2];
+    issue(blockIdx.x, st[0]);
+    if constexpr (IPW <= 4) {
+        // Unrolled over IPW items, with the look-ahead unconditional (past the
+        // last item, this item's rows again, unused): the two stages are never
+        // carried around a loop edge (register copies there would wait for
+        // the loads in flight) and each wait covers exactly the item in use.
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int cur = blockIdx.x + k * gridDim.x;
+            if (cur >= n_items) break;
+            const int nxt = cur + gridDim.x;
+            issue(nxt < n_items ? nxt : cur, st[(k + 1) & 1]);
+            compute(cur, st[k & 1]);
+        }
+        // beyond IPW items (not reached with the launch geometry): one at a time
+        for (int cur = blockIdx.x + IPW * gridDim.x; cur < n_items; cur += gridDim.x) {
+            issue(cur, st[0]);
+            compute(cur, st[0]);
+        }
+    } else {
+        // more items per workgroup (8 tokens): a loop, whose unrolled form
+        // would not fit the instruction cache
+        int item = blockIdx.x;
+        for (;;) {
+            const int next = item + gridDim.x;
+            if (next < n_items) issue(next, st[1]);
+            compute(item, st[0]);
+            if (next >= n_items) break;
+            item = next;
+            const int after = item + gridDim.x;
+            if (after < n_items) issue(after, st[0]);
+            compute(item, st[1]);
+            if (after >= n_items) break;
+            item = after;
+        }
     }
 }
 
@@ -549,24 +577,43 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     extern __shared__ u32x4 q2h[];                 // [pair][q][chunk] of 8 halves
     __shared__ float red[G::kWaves][RPB][MT];
     __shared__ float s2l[kMaxPairsExt];
+    __shared__ int32_t c_exp[kMaxPairs + 1], c_off[kMaxPairs + 2], c_src[kMaxPairsExt], c_tok[kMaxPairsExt];
+    __shared__ float c_w[kMaxPairsExt];            // router weight of each pair (1 for the shared expert's rows)
 
     const bool shared = a.sh.w2 != nullptr;
     const int P = a.M * a.K, Pe = P + (shared ? a.M : 0);   // routed pairs, plus the shared expert's rows
     const int n_act = min(*a.cp.n_act, min(a.E, P) + (shared ? 1 : 0));
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform (an SGPR), so that every read of the compaction below is a
+    // scalar load: its waits then never hold up the vector loads of h and of
+    // the weights, which are counted separately
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int li = lane % LPR, grp = lane / LPR;
     const int n = blockIdx.x * RPB + grp;
 
-    auto load_slot = [&](int slot, u32x4* wv, uint32_t* sv) {
-        const int ea = a.cp.act_experts[slot];
+    // The compaction, copied to LDS once: its loads go out first, so waiting
+    // for them never waits for the h rows or the weights issued after them.
+    // All loads below are unconditional (clamped indices), which keeps the
+    // count of loads in flight the same on every path.
+    const int nc = min(a.E, P) + (shared ? 1 : 0);
+    const int tid = threadIdx.x;
+    const int32_t ce = a.cp.act_experts[min(tid, nc - 1)];
+    const int32_t co = a.cp.offsets[min(tid, nc)];
+    const int32_t cs = a.cp.pair_src[min(tid, Pe - 1)];
+    const int32_t ct = a.cp.pair_token[min(tid, Pe - 1)];
+    const float cw = a.topk_w[min(tid, P - 1)];
+    const int last = max(n_act - 1, 0);
+    // a slot's loads: a wave-uniform expert base plus this lane's fixed offset
+    const uint32_t woff = (uint32_t)n * (I / 2) + (uint32_t)li * 16, soff = (uint32_t)n * CH + (uint32_t)li;
+    auto load_slot = [&](int ea_any, u32x4* wv, uint32_t* sv) {
+        const int ea = __builtin_amdgcn_readfirstlane(ea_any);
         const bool sh = shared && ea == kSharedExpert;
         const int e = min(max(ea, 0), a.E - 1);
-        const u32x4* row = (const u32x4*)((sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2)) + (size_t)n * (I / 2));
-        const uint8_t* sc = (sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH) + (size_t)n * CH;
+        const uint8_t* wb = sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
+        const uint8_t* sb = sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) wv[i] = load_stream(row + li + LPR * i);
+        for (int i = 0; i < CPL; ++i) wv[i] = load_stream(reinterpret_cast<const u32x4*>(wb + woff + LPR * 16 * i));
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) sv[i] = sc[li + LPR * i];
+        for (int i = 0; i < CPL; ++i) sv[i] = sb[soff + LPR * i];
     };
 
     // The intermediate in LDS as f16.  From h: a wave per (token, expert) row
@@ -580,15 +627,29 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
 #pragma unroll
         for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(wave + G::kWaves * j, Pe - 1));
     }
-    int slot = wave;
-    u32x4 wv[CPL];
-    uint32_t sv[CPL];
-    if (slot < n_act) load_slot(slot, wv, sv);
+    // two weight buffers used in turn (no register copies, which would wait
+    // for loads in flight): A holds this wave's first slot from here on
+    u32x4 wA[CPL], wB[CPL];
+    uint32_t sA[CPL], sB[CPL];
+    load_slot(a.cp.act_experts[min(wave, last)], wA, sA);   // a scalar load of the expert id
+    if (tid < nc) c_exp[tid] = ce;
+    if (tid <= nc) c_off[tid] = co;
+    if (tid < Pe) {
+        c_src[tid] = cs;
+        c_tok[tid] = ct;
+        c_w[tid] = tid < P ? cw : 1.0f;
+    }
 
     if constexpr (FROM_H) {
         _Float16* q16 = reinterpret_cast<_Float16*>(q2h);
         const bool tap = blockIdx.x == 0 && a.q2_out != nullptr;
-        for (int base = 0; base < Pe; base += G::kWaves * RB) {
+        // a compile-time trip count (at most MT (K + 1) rows) keeps the loop
+        // unrolled, so each wait covers exactly the rows it needs
+        constexpr int NIT = (MT * (kMaxTopK + 1) + G::kWaves * RB - 1) / (G::kWaves * RB);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int base = it * G::kWaves * RB;
+            if (base >= Pe) break;
             if (base > 0) {
 #pragma unroll
                 for (int j = 0; j < RB; ++j) rows[j].load(a.h, min(base + wave + G::kWaves * j, Pe - 1));
@@ -646,11 +707,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     float acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-    for (; slot < n_act; slot += G::kWaves) {
-        u32x4 nwv[CPL];
-        uint32_t nsv[CPL];
-        const int nslot = slot + G::kWaves;
-        if (nslot < n_act) load_slot(nslot, nwv, nsv);
+    auto consume = [&](int slot, const u32x4* wv, const uint32_t* sv) {
         half2_t hw[CPL * 16];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -659,10 +716,10 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
             e2m1x8_to_half(wv[i].z, hw + 16 * i + 8);
             e2m1x8_to_half(wv[i].w, hw + 16 * i + 12);
         }
-        const int q0 = min(max(a.cp.offsets[slot], 0), Pe), q1 = min(a.cp.offsets[slot + 1], Pe);
+        const int q0 = min(max(c_off[slot], 0), Pe), q1 = min(c_off[slot + 1], Pe);
         for (int qq = q0; qq < q1; ++qq) {
-            const int p = min(max(a.cp.pair_src[qq], 0), Pe - 1);
-            const int tok = a.cp.pair_token[qq];
+            const int p = min(max(c_src[qq], 0), Pe - 1);
+            const int tok = c_tok[qq];
             float d = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
@@ -672,17 +729,28 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
                 d += ldexp_e8m0(block_dot(hw + 16 * i, a0, a1, a2, a3), sv[i]);
             }
             d = group_sum<LPR>(d);
-            const float coef = (p < P ? a.topk_w[p] : 1.0f) * s2l[p];
+            const float coef = c_w[p] * s2l[p];
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 if (t == tok) acc[t] = fmaf(coef, d, acc[t]);
         }
-        if (nslot < n_act) {
+    };
+    // slots wave, wave + 8, ...: the next slot's weights load while this one
+    // is used (past the end, the current slot's rows load again, unused).
+    // The loop is unrolled over the most slots a wave can have, so each step
+    // is straight-line code whose waits cover exactly the slot in use.
+    constexpr int NS = (MT * (kMaxTopK + 1) + G::kWaves - 1) / G::kWaves;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                wv[i] = nwv[i];
-                sv[i] = nsv[i];
-            }
+    for (int k = 0; k < NS; ++k) {
+        const int slot = wave + G::kWaves * k;
+        if (slot >= n_act) break;
+        const int next = slot + G::kWaves < n_act ? slot + G::kWaves : slot;
+        if (k % 2 == 0) {
+            load_slot(c_exp[next], wB, sB);
+            consume(slot, wA, sA);
+        } else {
+            load_slot(c_exp[next], wA, sA);
+            consume(slot, wB, sB);
         }
     }
     if (li == 0) {

@@ -27,48 +27,81 @@ __device__ __forceinline__ float f32_from_orderable(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-K of one token's E logits by one wave, as K rounds of a wave-wide
-// maximum of the orderable logit: each round takes the largest remaining
-// value and, among the experts holding it, the lowest index (expert
-// e = lane + 64 i, so the first slot i whose ballot matches, at its lowest
-// lane), so the winners come out in canonical order (logit descending, lower
-// index first among equal logits).  A taken value is cleared to 0, below
-// every real value.  The weights are the softmax over the selected logits.
+// Top-K of one token's E logits by one wave.  Lane l holds the logits of
+// experts l + 64 i (slot i), as orderable keys, sorted once inside the lane
+// by (key descending, slot ascending).  Each of the K rounds takes the
+// wave-wide maximum of the lanes' first entries; the lane holding it (among
+// several lanes with an equal first key, the one whose expert index is
+// lowest) gives up that entry.  Since a lane's equal keys are in slot order,
+// the winners come out in canonical order: logit descending, lower expert
+// index first among equal logits.  The weights are the softmax over the
+// selected logits.
+template <int PER>
+__device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b)
+{
+    const bool sw = u[b] > u[a] || (u[b] == u[a] && s[b] < s[a]);
+    const uint32_t ua = u[a], ub = u[b];
+    const int sa = s[a], sb = s[b];
+    u[a] = sw ? ub : ua;
+    u[b] = sw ? ua : ub;
+    s[a] = sw ? sb : sa;
+    s[b] = sw ? sa : sb;
+}
+
 template <int PER>
 __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
     uint32_t u[PER];
+    int s[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {             // unconditional loads: all in flight together
         const int e = lane + kWave * i;
         const float v = L[e < E ? e : E - 1];
-        u[i] = (e < E) ? f32_orderable(v + 0.0f) : 0u;   // + 0.0f folds -0 into +0
+        u[i] = (e < E) ? f32_orderable(v + 0.0f) : 0u;   // + 0.0f folds -0 into +0; 0 is below every key
+        s[i] = i;
+    }
+    // sorting network over the lane's entries (a strict order: slots differ)
+    if constexpr (PER == 2) {
+        lane_sort_step<PER>(u, s, 0, 1);
+    } else if constexpr (PER == 4) {
+        lane_sort_step<PER>(u, s, 0, 1);
+        lane_sort_step<PER>(u, s, 2, 3);
+        lane_sort_step<PER>(u, s, 0, 2);
+        lane_sort_step<PER>(u, s, 1, 3);
+        lane_sort_step<PER>(u, s, 1, 2);
+    } else if constexpr (PER > 4) {              // odd-even transposition
+#pragma unroll
+        for (int ph = 0; ph < PER; ++ph)
+#pragma unroll
+            for (int a = ph & 1; a + 1 < PER; a += 2) lane_sort_step<PER>(u, s, a, a + 1);
     }
     uint32_t my_u = 0u;                         // lane r ends with the rank-r value and expert
     int my_e = 0;
     uint32_t top = 0u;
     for (int r = 0; r < K; ++r) {
-        uint32_t best = u[0];
-#pragma unroll
-        for (int i = 1; i < PER; ++i) best = max(best, u[i]);
-        const uint32_t m = wave_max_u32(best);
-        int wi = PER, wl = 0;
-#pragma unroll
-        for (int i = PER - 1; i >= 0; --i) {    // the lowest slot with a match wins
-            const uint64_t b = __ballot(u[i] == m);
-            if (b != 0ull) {
-                wi = i;
-                wl = (int)__builtin_ctzll(b);
-            }
+        const uint32_t m = wave_max_u32(u[0]);
+        const uint64_t b = __ballot(u[0] == m);
+        int wl = (int)__builtin_ctzll(b);
+        if (__popcll(b) > 1) {                  // equal first keys in several lanes (an exact tie)
+            const uint32_t cand = (u[0] == m) ? (uint32_t)(lane + kWave * s[0]) : 0xFFFFFFFFu;
+            wl = (int)(wave_min_u32(cand) & (kWave - 1));
         }
+        const int we = wl + kWave * __builtin_amdgcn_readlane(s[0], wl);
         if (r == 0) top = m;
         if (lane == r) {
             my_u = m;
-            my_e = wl + kWave * wi;
+            my_e = we;
         }
+        if (lane == wl) {                       // the winner gives up its first entry
 #pragma unroll
-        for (int i = 0; i < PER; ++i) u[i] = (i == wi && lane == wl) ? 0u : u[i];
+            for (int i = 0; i + 1 < PER; ++i) {
+                u[i] = u[i + 1];
+                s[i] = s[i + 1];
+            }
+            u[PER - 1] = 0u;
+            s[PER - 1] = PER;
+        }
     }
     const float lmax = f32_from_orderable(top);
     const float ex = (lane < K) ? expf(f32_from_orderable(my_u) - lmax) : 0.0f;

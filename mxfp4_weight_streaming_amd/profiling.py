@@ -20,7 +20,10 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
+# the gate/up kernel's code and its launch geometry
+KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/gemv_kernels.hpp",
+                  "mxfp4_weight_streaming_amd/csrc/moe_kernels.hip",
+                  "mxfp4_weight_streaming_amd/csrc/moe_types.hpp",
                   "mxfp4_weight_streaming_amd/csrc/device_common.hpp",
                   "mxfp4_weight_streaming_amd/csrc/topk_wave.hpp"]
 
