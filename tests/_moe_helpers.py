@@ -72,3 +72,19 @@ def fp8_code_mismatches_ok(gpu_q: np.ndarray, ref_q: np.ndarray, ref_y: np.ndarr
         if not (same_sign and adjacent and near):
             bad.append(i)
     return len(idx[0]), bad
+
+
+def requant_codes_match(q2, s2, h, rel: float = 1e-6):
+    """The kernel's FP8 intermediate (q2, s2) against the oracle's
+    requantisation of the kernel's own h: scales bit-exact; codes equal except
+    where h / s2 lies within `rel` of a rounding midpoint (the kernels
+    multiply by the correctly rounded reciprocal of s2 where the oracle
+    divides).  Returns the number of differing codes."""
+    import oracle
+    q2_own, s2_own = oracle.requant(h)
+    assert np.array_equal(np.asarray(s2, np.float32).view(np.uint32), s2_own.view(np.uint32))
+    y = (np.asarray(h, np.float32) / s2_own[:, None]).astype(np.float32)
+    n_mis, bad = fp8_code_mismatches_ok(q2, q2_own, y, rel=rel)
+    assert not bad, (n_mis, bad[:5])
+    return n_mis
+
