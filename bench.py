@@ -136,6 +136,7 @@ def main() -> int:
         ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
         wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
         n_active = torch.zeros((reps, L), dtype=torch.int32, device="cuda")
+        stream.wait_stream(torch.cuda.current_stream())   # inputs were made on the default stream
         with torch.cuda.stream(stream):
             for r in range(reps):
                 for l in range(L):
@@ -352,6 +353,7 @@ def lm_head_bench(args, moe, stream) -> dict:
     for M in (1, 4):
         x = (torch.randn((M, H), generator=g, device="cuda")).to(torch.bfloat16).view(torch.int16)
         logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+        stream.wait_stream(torch.cuda.current_stream())   # x was made on the default stream
         with torch.cuda.stream(stream):
             for i in range(20):
                 q, sc = copies[i % 2]
@@ -410,6 +412,7 @@ def chunk_bench(args, moe, synth, stack, shp, stream) -> dict:
     ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
     wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
     n_active = torch.zeros(L, dtype=torch.int32, device="cuda")
+    stream.wait_stream(torch.cuda.current_stream())       # inputs were made on the default stream
     with torch.cuda.stream(stream):
         for l in range(L):
             moe.moe_route(shp, M, xs[l], routers[l], ids, wts, ws, taps={"n_active": n_active[l:l + 1]})

@@ -14,6 +14,7 @@ the kernel source it was measured on.
 from __future__ import annotations
 
 import csv
+import json
 import hashlib
 import os
 import statistics
@@ -95,9 +96,61 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, out_path: str, fetch_
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
+def phases(trace_csv: str, out_path: str, kernel_prefix: str, sizes, names) -> None:
+    """Appends to out_path the mean and median duration of one kernel's
+    dispatches in each phase of the bench run, in dispatch order (phase i
+    holds the next sizes[i] dispatches)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if r["Kernel_Name"].startswith(kernel_prefix)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    lines = ["", f"per-phase durations of {_short(kernel_prefix)} (us), in dispatch order:"]
+    at = 0
+    for n, name in zip(sizes, names):
+        seg = d[at:at + n]
+        at += n
+        if seg:
+            lines.append(f"  {name:32s} n={len(seg):5d} mean={statistics.mean(seg):8.3f} median={statistics.median(seg):8.3f}")
+    open(out_path, "a").write("\n".join(lines) + "\n")
+
+
+def sweep(out_path: str, runs) -> None:
+    """Writes a token-sweep table from bench.py JSON lines: runs is a list of
+    (command, json_path) pairs."""
+    lines = ["# Decode token sweep (bench.py, one MI355X, cold walk over independent layers, HIP graph replay)"]
+    lines += [f"command: {cmd}" for cmd, _ in runs]
+    lines += ["table: python3 -m mxfp4_weight_streaming_amd.profiling sweep <this file> <command> <its JSON line> ..."]
+    lines += ["timing: HIP events around the graph replays; GB/s = algorithmic bytes (selected experts' MXFP4 codes "
+              "+ scales, bf16 router, x, out) / time; kernel columns: start/stop events stamped by each launch", "",
+              f"{'experts':>7s} {'tokens':>6s} {'distinct':>8s} {'us/layer':>9s} {'GB/s':>7s} {'%8TB/s':>7s} "
+              f"{'router':>7s} {'gate_up':>8s} {'down':>7s}"]
+    chunks = []
+    for _, path in runs:
+        d = json.loads(open(path).read().strip().splitlines()[-1])
+        E = d["config"]["experts"]
+        for M, r in sorted(d["by_tokens"].items(), key=lambda kv: int(kv[0])):
+            k = r["kernel_us"]
+            lines.append(f"{E:7d} {int(M):6d} {r['mean_distinct_experts']:8.2f} {r['us_per_layer']:9.2f} {r['gbs']:7.0f} "
+                         f"{r['pct_of_hbm_peak']:7.2f} {k['router']:7.2f} {k['gate_up']:8.2f} {k['down']:7.2f}")
+        if d.get("chunk"):
+            c = d["chunk"]
+            chunks.append(f"{c['tokens']}-token chunk, {E} experts: {c['us_per_layer']:.2f} us/layer, {c['gbs']:.1f} GB/s, "
+                          f"{c['mean_experts_touched']:.1f} experts touched, kernels (us) {c['kernel_us']}, matrix cores "
+                          f"{c['mfma']['tflops_layer']:.1f} TFLOP/s")
+    lines += [""] + chunks
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+    elif sys.argv[1] == "phases":
+        # phases TRACE OUT KERNEL_PREFIX name=count name=count ...
+        pairs = [a.split("=") for a in sys.argv[5:]]
+        phases(sys.argv[2], sys.argv[3], sys.argv[4], [int(c) for _, c in pairs], [n for n, _ in pairs])
+    elif sys.argv[1] == "sweep":
+        # sweep OUT CMD1 JSON1 [CMD2 JSON2 ...]
+        rest = sys.argv[3:]
+        sweep(sys.argv[2], list(zip(rest[0::2], rest[1::2])))
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6], sys.argv[7])
     else:
