@@ -83,56 +83,43 @@ struct alignas(16) RouteLds {
     int32_t offsets[kMaxPairs + 2];
     int32_t pair_token[kMaxPairsExt];
     int32_t pair_src[kMaxPairsExt];
+    int32_t sorted_e[kMaxPairs];                // compaction scratch: expert at each position
 };
 
-// One wave; lane p < P owns pair p with expert e_p.  Its compacted position
-// is the number of pairs ahead of it in (expert, pair index) order; a pair
-// that is its expert's first gets slot = number of distinct smaller experts.
-// The ids (at most PMAX) are read once with broadcast LDS loads.
+// One wave; lane p < P owns pair p, its expert e_p and the key e_p * 64 + p
+// (keys are distinct).  The pair's position in (expert, pair index) order is
+// the number of smaller keys, counted against each pair's key read as a
+// scalar.  The pairs are stored at their positions; a position opens a slot
+// when its expert differs from the previous position's, and slots are
+// numbered by counting the opening positions below.
 template <int PMAX>
 __device__ void compact_wave_t(int P, int K, RouteLds& r)
 {
     const int lane = threadIdx.x & 63;
-    constexpr int NV = (PMAX + 3) / 4;
-    int4 ids4[NV];
+    const int e = r.ids[min(lane, P - 1)];
+    const uint32_t key = lane < P ? (uint32_t)e * 64u + (uint32_t)lane : 0xFFFFFFFFu;
+    int pos = 0;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)       // unconditional: entries past P are ignored below
-        ids4[v] = *reinterpret_cast<const int4*>(r.ids + 4 * v);
-    const int e = (lane < P) ? r.ids[lane] : 0;
-    int pos = 0, same_before = 0;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = 4 * v + u;
-            const bool in = q < P;
-            pos += in && ((eq[u] < e) || (eq[u] == e && q < lane));
-            same_before += in && (eq[u] == e) && (q < lane);
-        }
-    }
-    const bool first = lane < P && same_before == 0;
-    const uint64_t firsts = __ballot(first);
-    int slot = 0;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int eq[4] = {ids4[v].x, ids4[v].y, ids4[v].z, ids4[v].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = 4 * v + u;
-            slot += (q < P) && ((firsts >> q) & 1ull) && eq[u] < e;
-        }
-    }
+    for (int q = 0; q < PMAX; ++q) pos += (uint32_t)__builtin_amdgcn_readlane((int)key, q) < key ? 1 : 0;
     if (lane < P) {
+        r.sorted_e[pos] = e;
         r.pair_token[pos] = lane / K;
         r.pair_src[pos] = lane;
-        if (first) {
-            r.act_experts[slot] = e;
-            r.offsets[slot] = pos;
-        }
+    }
+    // the stores above are read back by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const int i = min(lane, P - 1);
+    const int se = r.sorted_e[i], prev = r.sorted_e[max(i - 1, 0)];
+    const bool open = lane < P && (lane == 0 || se != prev);
+    const uint64_t opens = __ballot(open);
+    const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(opens >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)opens, 0u));
+    if (open) {
+        r.act_experts[slot] = se;
+        r.offsets[slot] = lane;
     }
     if (lane == 0) {
-        const int n = __popcll(firsts);
+        const int n = __popcll(opens);
         r.n_act = n;
         r.offsets[n] = P;
     }
@@ -226,9 +213,13 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Router: logits[t,e] = x[t] . Wr[e] in fp32 (exact bf16 products), one wave
-// per expert row with 16-byte loads; each workgroup also quantises a slice of
-// every token.
+// Router: logits[t,e] = x[t] . Wr[e] in fp32 (exact bf16 products).  One
+// workgroup per expert row: thread c holds the 16-byte chunk c (8 values) of
+// the row and of every token, so a workgroup sees every token whole and finds
+// its amax with 8 values per thread; the per-thread partial dot products and
+// maxima are reduced on DPP within rows of 16 lanes and then in LDS in a fixed
+// order.  The activation quantisation (chunk, token) items are spread over
+// the threads of the whole grid, one item each.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dot_bf16x8(u32x4 x, u32x4 w, float acc)
 {
@@ -243,65 +234,89 @@ __device__ __forceinline__ float dot_bf16x8(u32x4 x, u32x4 w, float acc)
     return acc;
 }
 
+// Largest |value| of 8 bf16 (NaN inputs are skipped, as by fmaxf).
+__device__ __forceinline__ float amax_bf16x8(u32x4 x)
+{
+    float m = fmaxf(fabsf(__uint_as_float(x.x << 16)), fabsf(__uint_as_float(x.x & 0xFFFF0000u)));
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(x.y << 16)), fabsf(__uint_as_float(x.y & 0xFFFF0000u))));
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(x.z << 16)), fabsf(__uint_as_float(x.z & 0xFFFF0000u))));
+    return fmaxf(m, fmaxf(fabsf(__uint_as_float(x.w << 16)), fabsf(__uint_as_float(x.w & 0xFFFF0000u))));
+}
+
+// Maximum over aligned rows of 16 lanes; every lane of a row gets it.
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    return fmaxf(v, dpp_f32<kDppMirror>(v));
+}
+
 template <int H, int MT>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a)
+__global__ __launch_bounds__(router_threads(H)) void router_kernel(RouterArgs a)
 {
     constexpr int NCH = H / 8;                       // 16-byte chunks per row
-    constexpr int CPL = (NCH + kWave - 1) / kWave;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
-    auto valid = [&](int i) { return NCH % kWave == 0 || lane + kWave * i < NCH; };
+    constexpr int NT = router_threads(H);
+    constexpr int NR = NT / 16;                      // rows of 16 lanes
+    __shared__ float red_dot[MT][NR], red_max[MT][NR];
+    __shared__ float s_tok[MT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int e = blockIdx.x;                        // the grid is one workgroup per expert
+    const int M = a.M;
+    const bool own = tid < NCH;
+    const int c = own ? tid : NCH - 1;               // past the row: a copy of the last chunk, counted nowhere
 
-    // issue every load up front: the router row, each token's hidden state and
-    // this workgroup's quantisation slice
-    u32x4 wv[CPL];
-    if (e < a.E) {
+    // every load first, unconditional (clamped): the row chunk, every token's
+    // chunk and this thread's quantisation item (chunk qi of the [M,H] array)
+    const u32x4 w = load_stream(reinterpret_cast<const u32x4*>(a.wr + (size_t)e * H) + c);
+    u32x4 xv[MT];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            if (valid(i)) wv[i] = load_stream((const u32x4*)(a.wr + (size_t)e * H) + lane + kWave * i);
-    }
-    u32x4 xv[MT][CPL];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            xv[t][i] = (t < a.M && valid(i)) ? *((const u32x4*)(a.x + (size_t)t * H) + lane + kWave * i)
-                                             : u32x4{0u, 0u, 0u, 0u};
-    const int per = (H + gridDim.x - 1) / gridDim.x;
-    const int kq = blockIdx.x * per + threadIdx.x;
-    const bool quant = a.act_q != nullptr && threadIdx.x < per && kq < H;
-    uint32_t xq[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) xq[t] = (quant && t < a.M) ? a.x[(size_t)t * H + kq] : 0u;
+    for (int t = 0; t < MT; ++t) xv[t] = *(reinterpret_cast<const u32x4*>(a.x + (size_t)min(t, M - 1) * H) + c);
+    const int nq = a.act_q != nullptr ? NCH * M : 0;
+    const int qi = blockIdx.x + gridDim.x * tid;
+    const u32x4 xq = *(reinterpret_cast<const u32x4*>(a.x) + min(qi, NCH * M - 1));
 
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        if (t >= a.M) continue;
-        if (e < a.E) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                if (valid(i)) acc = dot_bf16x8(xv[t][i], wv[i], acc);
-            const float sum = wave_sum(acc);
-            if (lane == 0) a.logits[(size_t)t * a.E + e] = sum;
-        }
-        if (a.act_q != nullptr) {
-            // every wave holds the whole token, so every wave finds the same amax
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].x << 16)), fabsf(__uint_as_float(xv[t][i].x & 0xFFFF0000u))));
-                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].y << 16)), fabsf(__uint_as_float(xv[t][i].y & 0xFFFF0000u))));
-                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].z << 16)), fabsf(__uint_as_float(xv[t][i].z & 0xFFFF0000u))));
-                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(xv[t][i].w << 16)), fabsf(__uint_as_float(xv[t][i].w & 0xFFFF0000u))));
-            }
-            const float amax = wave_max(m);
-            const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-            if (quant) a.act_q[(size_t)t * H + kq] = (uint8_t)e4m3_encode(bf16_bits_to_f32(xq[t]) / s);
-            if (blockIdx.x == 0 && threadIdx.x == 0) a.act_s[t] = s;
+        const float d = group_sum<16>(own ? dot_bf16x8(xv[t], w, 0.0f) : 0.0f);
+        const float m = row16_max(own ? amax_bf16x8(xv[t]) : 0.0f);
+        if ((lane & 15) == 0) {
+            red_dot[t][tid >> 4] = d;
+            red_max[t][tid >> 4] = m;
         }
     }
-
+    __syncthreads();
+    if (tid < MT) {
+        float d = 0.0f, m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            d += red_dot[tid][r];
+            m = fmaxf(m, red_max[tid][r]);
+        }
+        const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
+        s_tok[tid] = s;
+        if (tid < M) {
+            a.logits[(size_t)tid * a.E + e] = d;
+            if (blockIdx.x == 0 && a.act_q != nullptr) a.act_s[tid] = s;
+        }
+    }
+    if (nq == 0) return;
+    __syncthreads();
+    auto quantise = [&](int item, u32x4 v) {
+        const float s = s_tok[item / NCH];
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+        uint32_t code[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
+            code[j >> 2] |= e4m3_encode(__uint_as_float(b) / s) << (8 * (j & 3));
+        }
+        *reinterpret_cast<u32x2*>(a.act_q + (size_t)item * 8) = u32x2{code[0], code[1]};
+    };
+    if (qi < nq) quantise(qi, xq);
+    // more items than threads in the grid (few experts): one at a time
+    for (int q = qi + gridDim.x * NT; q < nq; q += gridDim.x * NT)
+        quantise(q, *(reinterpret_cast<const u32x4*>(a.x) + q));
 }
 
 // ---------------------------------------------------------------------------

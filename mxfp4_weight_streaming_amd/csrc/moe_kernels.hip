@@ -38,10 +38,8 @@ hipError_t launch_router(int H, int mt, const RouterArgs& a, hipStream_t s, cons
 {
     const Kern k = find_kernel(key_router(H, mt));
     if (!k.ok()) return hipErrorInvalidDeviceFunction;
-    // one wave per expert row; workgroup t also quantises token t, so there
-    // are at least M workgroups
-    const int blocks = (a.E + 3) / 4 > a.M ? (a.E + 3) / 4 : a.M;
-    return launch_kern(k, dim3(blocks), dim3(256), 0, s, ev, a);
+    // one workgroup per expert row, one thread per 16-byte chunk of it
+    return launch_kern(k, dim3(a.E), dim3(router_threads(H)), 0, s, ev, a);
 }
 
 hipError_t launch_quant(int H, const uint16_t* x, int M, uint8_t* q, float* sc, hipStream_t s)

@@ -180,6 +180,10 @@ struct CombineArgs {
 // ---------------------------------------------------------------------------
 constexpr int kWaveSize = 64;
 
+// Router GEMV: one workgroup per expert row, one thread per 16-byte chunk
+// (8 bf16) of the row, rounded up to whole waves.
+__host__ __device__ constexpr int router_threads(int H) { return ((H / 8 + kWaveSize - 1) / kWaveSize) * kWaveSize; }
+
 // gate/up GEMV: H/32 chunks of 16 code bytes per row, LPR lanes per row.
 __host__ __device__ constexpr int gate_up_lanes_per_row(int H)
 {
