@@ -72,9 +72,10 @@
  * kernels a call would run so that callers can check at startup that the path
  * they expect is active, as the pages advise.  Non-finite inputs are not
  * detected; results for them are unspecified.  Caller-given topk_ids must
- * lie in [0, E) and be distinct within a token; other ids give unspecified
- * results (they are clamped on the device, never read or written out of
- * bounds).
+ * lie in [0, E) and, for M <= 8, be distinct within a token.  For M > 8 a
+ * token may also name one expert more than once: each (token, j) pair is then
+ * computed and weighted on its own.  Other ids give unspecified results (they
+ * are clamped on the device, never read or written out of bounds).
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H

@@ -163,31 +163,44 @@ __global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
 
 // ---------------------------------------------------------------------------
 // Expert-major ordering of the M*K (token, slot) pairs by one workgroup.  The
-// pairs of an expert end up contiguous and in ascending token order (the
-// decode path's compaction order); active experts get slots in ascending id.
-// When every token's K ids are distinct (always so for routed ids), each
-// expert gets an M-bit token mask in LDS and a pair's rank inside its expert
-// is a popcount of the mask below its token.  Caller ids that repeat an
-// expert inside one token take a bitonic sort of (expert << 16 | pair) keys.
-// The rows of every slot are then cut into chunks of at most kChunkRows rows
-// for the grouped kernels, 4-tile chunks first, then 3-, 2- and 1-tile ones.
+// pairs of an expert end up contiguous and in (token, slot) order (the decode
+// path's compaction order); active experts get slots in ascending id.  Each
+// expert gets an M-bit token mask in LDS; when no token names an expert twice
+// (always so for routed ids) the masks' popcounts are the expert counts and a
+// pair's rank inside its expert is a popcount of the mask below its token.
+// A token naming an expert more than once shows as a popcount total below
+// M*K; such ids take exact counts and a bitonic sort of (expert << 16 | pair)
+// keys.  The rows of every slot are then cut into chunks of at most
+// kChunkRows rows for the grouped kernels, 4-tile chunks first, then 3-, 2-
+// and 1-tile ones.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
+constexpr int kSortPairsPerThread = kMaxChunkPairs / kSortThreads;
+
+// Inclusive prefix sum over the wave on DPP: shifts by 1, 2, 4 and 8 within
+// rows of 16 lanes, then each row adds the totals of the rows before it.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+    return v;
+}
 
 // Exclusive prefix sum of one value per thread over the workgroup, in thread
-// order; every thread must call it.
+// order; every thread must call it.  Values may pack several counters in
+// separate bit fields, as long as no field's total overflows it.
 __device__ int block_excl_scan(int v, int* tmp, int& total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == kWave - 1) tmp[w] = x;
     __syncthreads();
     int base = 0, tot = 0;
+#pragma unroll
     for (int i = 0; i < kSortThreads / kWave; ++i) {
         const int t = tmp[i];
         base += (i < w) ? t : 0;
@@ -204,34 +217,55 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t pre[kMaxExperts];
     __shared__ int32_t tmp[kSortThreads / kWave];
-    __shared__ int32_t dup;
     const int P = a.M * a.K, K = a.K, E = a.E, W = (a.M + 31) >> 5;
     const int tid = threadIdx.x;
     auto clamp_e = [&](int e) { return e < 0 ? 0 : (e >= E ? E - 1 : e); };
-    if (tid == 0) dup = 0;
-    for (int e = tid; e < kMaxExperts; e += kSortThreads) cnt[e] = 0;
+    // every pair's expert, loaded once (all loads first)
+    int eid[kSortPairsPerThread];
+#pragma unroll
+    for (int i = 0; i < kSortPairsPerThread; ++i) {
+        const int p = tid + kSortThreads * i;
+        eid[i] = clamp_e(a.ids[p < P ? p : P - 1]);
+    }
     for (int i = tid; i < E * W; i += kSortThreads) sh[i] = 0u;
     __syncthreads();
-    for (int p = tid; p < P; p += kSortThreads) {
-        const int t = p / K, j = p - t * K;
-        const int e = clamp_e(a.ids[p]);
-        bool d = false;
-        for (int jj = 0; jj < j; ++jj) d |= clamp_e(a.ids[t * K + jj]) == e;
-        if (d) dup = 1;
-        atomicOr(&sh[e * W + (t >> 5)], 1u << (t & 31));
-        atomicAdd(&cnt[e], 1);
+#pragma unroll
+    for (int i = 0; i < kSortPairsPerThread; ++i) {
+        const int p = tid + kSortThreads * i;
+        if (p < P) {
+            const int t = p / K;
+            atomicOr(&sh[eid[i] * W + (t >> 5)], 1u << (t & 31));
+        }
     }
     __syncthreads();
-    // expert offsets and slots (one thread per expert; thread E stands for the
-    // shared expert, whose M rows follow the routed pairs in one more slot)
+    // per expert (thread e < E; thread E stands for the shared expert, whose M
+    // rows follow the routed pairs in one more slot): its count, and with it
+    // whether it is active; one scan gives offsets (low 16 bits) and slots
+    int c = 0;
+    if (tid < E)
+        for (int w = 0; w < W; ++w) c += __popc(sh[tid * W + w]);
     const bool virt = a.shared != 0 && tid == E;
-    const int c = (tid < E) ? cnt[tid] : (virt ? a.M : 0);
-    int total_pairs = 0, n_act = 0;
-    const int off_e = block_excl_scan(c, tmp, total_pairs);
-    const int slot_e = block_excl_scan(c > 0 ? 1 : 0, tmp, n_act);
+    const int extra = a.shared != 0 ? a.M : 0;
+    int total = 0;
+    int cc = (tid < E) ? c : (virt ? a.M : 0);
+    int packed = block_excl_scan(((cc > 0 ? 1 : 0) << 16) | cc, tmp, total);
+    const bool dup = (total & 0xFFFF) - extra != P;      // uniform: some token names an expert twice
+    if (dup) {
+        // exact counts (the masks hold each (token, expert) once)
+        for (int e = tid; e < kMaxExperts; e += kSortThreads) cnt[e] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortPairsPerThread; ++i)
+            if (tid + kSortThreads * i < P) atomicAdd(&cnt[eid[i]], 1);
+        __syncthreads();
+        cc = (tid < E) ? cnt[tid] : (virt ? a.M : 0);
+        packed = block_excl_scan(((cc > 0 ? 1 : 0) << 16) | cc, tmp, total);
+    }
+    const int off_e = packed & 0xFFFF, slot_e = packed >> 16;
+    const int total_pairs = total & 0xFFFF, n_act = total >> 16;
     const int rec_e = virt ? kSharedExpert : tid;
     if (tid < E) pre[tid] = off_e;
-    if (c > 0) {
+    if (cc > 0) {
         a.cp.act_experts[slot_e] = rec_e;
         a.cp.offsets[slot_e] = off_e;
     }
@@ -247,22 +281,24 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
         }
     }
     __syncthreads();
-    if (dup == 0) {
-        for (int p = tid; p < P; p += kSortThreads) {
-            const int t = p / K;
-            const int e = clamp_e(a.ids[p]);
-            const uint32_t* mrow = sh + e * W;
-            int rank = __popc(mrow[t >> 5] & ((1u << (t & 31)) - 1u));
-            for (int w = 0; w < (t >> 5); ++w) rank += __popc(mrow[w]);
-            const int pos = pre[e] + rank;
-            a.cp.pair_token[pos] = t;
-            a.cp.pair_src[pos] = p;
-            a.pos_of[p] = pos;
+    if (!dup) {
+#pragma unroll
+        for (int i = 0; i < kSortPairsPerThread; ++i) {
+            const int p = tid + kSortThreads * i;
+            if (p < P) {
+                const int t = p / K;
+                const uint32_t* mrow = sh + eid[i] * W;
+                int rank = __popc(mrow[t >> 5] & ((1u << (t & 31)) - 1u));
+                for (int w = 0; w < (t >> 5); ++w) rank += __popc(mrow[w]);
+                const int pos = pre[eid[i]] + rank;
+                a.cp.pair_token[pos] = t;
+                a.cp.pair_src[pos] = p;
+                a.pos_of[p] = pos;
+            }
         }
     } else {
         int NP = 64;
         while (NP < P) NP <<= 1;
-        __syncthreads();
         for (int i = tid; i < NP; i += kSortThreads)
             sh[i] = (i < P) ? (((uint32_t)clamp_e(a.ids[i]) << 16) | (uint32_t)i) : 0xFFFFFFFFu;
         __syncthreads();
@@ -288,19 +324,20 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
             a.pos_of[p] = pos;
         }
     }
-    // chunk list, from the expert's own thread (its count c and slot_e): its
-    // 4-tile chunks first, then its last chunk in the group of its tile count
-    const int rem = c % kChunkRows;
-    const int full = c / kChunkRows + (rem > 3 * 16 ? 1 : 0);
+    // chunk list, from the expert's own thread (its count cc and slot_e): its
+    // 4-tile chunks first, then its last chunk in the group of its tile count;
+    // two scans, each packing two counters
+    const int rem = cc % kChunkRows;
+    const int full = cc / kChunkRows + (rem > 3 * 16 ? 1 : 0);
     const int last_tiles = (rem > 0 && rem <= 3 * 16) ? (rem + 15) / 16 : 0;
-    int n4 = 0, n3 = 0, n2 = 0, n1 = 0;
-    const int at4 = block_excl_scan(full, tmp, n4);
-    const int at3 = block_excl_scan(last_tiles == 3 ? 1 : 0, tmp, n3);
-    const int at2 = block_excl_scan(last_tiles == 2 ? 1 : 0, tmp, n2);
-    const int at1 = block_excl_scan(last_tiles == 1 ? 1 : 0, tmp, n1);
-    if (c > 0) {
+    int t43 = 0, t21 = 0;
+    const int s43 = block_excl_scan((full << 16) | (last_tiles == 3 ? 1 : 0), tmp, t43);
+    const int s21 = block_excl_scan(((last_tiles == 2 ? 1 : 0) << 16) | (last_tiles == 1 ? 1 : 0), tmp, t21);
+    const int at4 = s43 >> 16, at3 = s43 & 0xFFFF, at2 = s21 >> 16, at1 = s21 & 0xFFFF;
+    const int n4 = t43 >> 16, n3 = t43 & 0xFFFF, n2 = t21 >> 16, n1 = t21 & 0xFFFF;
+    if (cc > 0) {
         for (int k = 0; k < full; ++k) {
-            const int rows = c - k * kChunkRows;
+            const int rows = cc - k * kChunkRows;
             a.chunks.rec[at4 + k] = make_int4(rec_e, off_e + k * kChunkRows, rows < kChunkRows ? rows : kChunkRows, 0);
         }
         if (last_tiles > 0) {

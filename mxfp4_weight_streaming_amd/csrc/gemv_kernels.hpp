@@ -145,9 +145,11 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
     }
     __syncthreads();
     if (wave == 0) {
-        if (M == 1) {
-            // one token: its K experts are distinct, so the slots are the
-            // experts in ascending id and slot s holds exactly one pair
+        if (M == 1 && src.logits != nullptr) {
+            // one token routed here: its K experts are distinct, so the slots
+            // are the experts in ascending id and slot s holds exactly one
+            // pair (caller ids may repeat an expert: they take the general
+            // compaction)
             const int lane = tid & 63;
             const int4 a4 = *reinterpret_cast<const int4*>(r.ids), b4 = *reinterpret_cast<const int4*>(r.ids + 4);
             const int all[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
