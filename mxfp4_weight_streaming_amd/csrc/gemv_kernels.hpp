@@ -261,7 +261,6 @@ __global__ __launch_bounds__(router_threads(H)) void router_kernel(RouterArgs a)
     constexpr int NT = router_threads(H);
     constexpr int NR = NT / 16;                      // rows of 16 lanes
     __shared__ float red_dot[MT][NR], red_max[MT][NR];
-    __shared__ float s_tok[MT];
     const int tid = threadIdx.x, lane = tid & 63;
     const int e = blockIdx.x;                        // the grid is one workgroup per expert
     const int M = a.M;
@@ -288,24 +287,23 @@ __global__ __launch_bounds__(router_threads(H)) void router_kernel(RouterArgs a)
         }
     }
     __syncthreads();
-    if (tid < MT) {
-        float d = 0.0f, m = 0.0f;
+    // token t's scale, found by every thread that needs it from the row maxima
+    // (max is exact in any order, so all find the same value)
+    auto token_scale = [&](int t) {
+        float m = 0.0f;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            d += red_dot[tid][r];
-            m = fmaxf(m, red_max[tid][r]);
-        }
-        const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
-        s_tok[tid] = s;
-        if (tid < M) {
-            a.logits[(size_t)tid * a.E + e] = d;
-            if (blockIdx.x == 0 && a.act_q != nullptr) a.act_s[tid] = s;
-        }
+        for (int r = 0; r < NR; ++r) m = fmaxf(m, red_max[t][r]);
+        return (m == 0.0f) ? 1.0f : m / 448.0f;
+    };
+    if (tid < M) {
+        float d = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) d += red_dot[tid][r];
+        a.logits[(size_t)tid * a.E + e] = d;
+        if (blockIdx.x == 0 && a.act_q != nullptr) a.act_s[tid] = token_scale(tid);
     }
-    if (nq == 0) return;
-    __syncthreads();
     auto quantise = [&](int item, u32x4 v) {
-        const float s = s_tok[item / NCH];
+        const float s = token_scale(item / NCH);
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t code[2] = {0u, 0u};
 #pragma unroll
@@ -354,28 +352,64 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane % LPR, grp = lane / LPR;
 
-    // 0. every token's activations as f16 in LDS (independent of the routing,
-    //    so these loads overlap the routing prologue's); all loads first
+    // 0. every token's activations as f16 in LDS.  From FP8 codes (act_q):
+    //    their loads go out first and overlap the routing prologue.  From the
+    //    bf16 hidden state of one token (x): waves 1-3 quantise it while wave
+    //    0 derives the routing, each reading the whole token so that they
+    //    agree on its amax without a barrier (the same arithmetic as the
+    //    router's quantisation: s = amax / 448, codes E4M3(x / s)).
+    const bool from_x = a.x != nullptr;                 // one token only
     constexpr int NST = (MT * (H / 8) + 255) / 256;
     const int n8 = M * (H / 8);
     u32x2 stg[NST];
+    float s_tok = 0.0f;
+    if (!from_x) {
 #pragma unroll
-    for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
-    const float s_tok = a.act_s[min((int)threadIdx.x, M - 1)];
+        for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
+        s_tok = a.act_s[min((int)threadIdx.x, M - 1)];
+    } else if (wave != 0) {
+        constexpr int NC8 = H / 8, CPL8 = (NC8 + kWave - 1) / kWave;   // 16-byte chunks of the token
+        u32x4 xv[CPL8];
+#pragma unroll
+        for (int i = 0; i < CPL8; ++i) xv[i] = reinterpret_cast<const u32x4*>(a.x)[min(lane + kWave * i, NC8 - 1)];
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL8; ++i)
+            if (lane + kWave * i < NC8) m = fmaxf(m, amax_bf16x8(xv[i]));
+        m = wave_max(m);
+        const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
+#pragma unroll
+        for (int i = 0; i < CPL8; ++i) {
+            const int c = lane + kWave * i;
+            if (c < NC8 && i % 3 == wave - 1) {
+                const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                uint32_t code[2] = {0u, 0u};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
+                    code[j >> 2] |= e4m3_encode(__uint_as_float(b) / s) << (8 * (j & 3));
+                }
+                act[(c & 3) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
+            }
+        }
+        if (wave == 1 && lane == 0) act_sl[0] = s;
+    }
     // 1. routing, derived independently by every workgroup (the staging loads
     //    above are in flight meanwhile); workgroup 0 publishes it for the down
     //    kernel (and the caller)
     route_prologue(a.src, rl);
     if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
+    if (!from_x) {
 #pragma unroll
-    for (int j = 0; j < NST; ++j) {
-        const int idx = threadIdx.x + 256 * j;
-        if (idx < n8) {
-            const int t = idx / (H / 8), g8 = idx % (H / 8);
-            act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+        for (int j = 0; j < NST; ++j) {
+            const int idx = threadIdx.x + 256 * j;
+            if (idx < n8) {
+                const int t = idx / (H / 8), g8 = idx % (H / 8);
+                act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+            }
         }
+        if ((int)threadIdx.x < M) act_sl[threadIdx.x] = s_tok;
     }
-    if ((int)threadIdx.x < M) act_sl[threadIdx.x] = s_tok;
     __syncthreads();
     const int n_items = rl.n_act * BPE;
 

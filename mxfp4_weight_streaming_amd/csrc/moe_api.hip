@@ -167,12 +167,12 @@ moe_status enqueue_topk(const moe_shape* s, int32_t M, bool from_logits, const i
 moe_status enqueue_gate_up(const moe_shape* s, int32_t M, const int32_t* ids, int32_t* ids_out, float* w_out,
                            const uint8_t* act_q, const float* act_s, const uint8_t* w13, const uint8_t* s13, float* h,
                            const Carved& c, hipStream_t st, const moe::LaunchEvents& ev = {},
-                           const moe::SharedWeights& sh = {})
+                           const moe::SharedWeights& sh = {}, const uint16_t* x = nullptr)
 {
     const int shared = has_shared(sh) ? 1 : 0;
     const moe::RouteSrc src{M, s->num_experts, s->topk, ids == nullptr ? c.at<float>(c.L.logits) : nullptr, ids,
                             shared};
-    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, sh};
+    moe::GateUpArgs a{src, ids_out, w_out, c.cp(), w13, s13, act_q, act_s, h, sh, x};
     hipError_t e = moe::launch_gate_up(s->hidden, s->inter, token_bound(M), num_slots(s, M) + shared, a, st, ev);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate_up launch");
 }
@@ -331,8 +331,16 @@ moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hid
         if ((st = enqueue_sort(shape, M, ids, c, s, has_shared(sh))) != MOE_OK) return st;
         return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2), sh);
     }
-    if ((st = enqueue_router(shape, M, hidden, router_w, q, sc, c, s, ev(0))) != MOE_OK) return st;
-    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, c, s, ev(1), sh)) != MOE_OK)
+    // One token: the gate/up kernel quantises the activations itself (its
+    // idle waves do it during the routing prologue), so the router only
+    // computes logits.  More tokens: the router quantises them, a slice per
+    // workgroup.
+    const bool one = M == 1;
+    if ((st = enqueue_router(shape, M, hidden, router_w, one ? nullptr : q, one ? nullptr : sc, c, s, ev(0))) !=
+        MOE_OK)
+        return st;
+    if ((st = enqueue_gate_up(shape, M, nullptr, ids, w, q, sc, w13, w13_scale, h, c, s, ev(1), sh,
+                              one ? hidden : nullptr)) != MOE_OK)
         return st;
     return enqueue_down(shape, M, h, nullptr, nullptr, nullptr, nullptr, w, w2, w2_scale, out, c, s, ev(2), sh);
 }

@@ -79,6 +79,8 @@ struct GateUpArgs {
     const float* act_s;    // [M]
     float* h;              // [M*K (+M),I]
     SharedWeights sh;      // read when the compaction holds the shared slot
+    const uint16_t* x;     // [1,H] bf16, or nullptr.  When set (one token), the
+                           // kernel quantises x itself and act_q/act_s are unused
 };
 
 struct DownArgs {
