@@ -354,11 +354,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 
     // 0. every token's activations as f16 in LDS.  From FP8 codes (act_q):
     //    their loads go out first and overlap the routing prologue.  From the
-    //    bf16 hidden state of one token (x): waves 1-3 quantise it while wave
-    //    0 derives the routing, each reading the whole token so that they
-    //    agree on its amax without a barrier (the same arithmetic as the
-    //    router's quantisation: s = amax / 448, codes E4M3(x / s)).
-    const bool from_x = a.x != nullptr;                 // one token only
+    //    bf16 hidden states of one or two tokens (x): the waves from M on
+    //    quantise them while waves 0..M-1 derive the routing, each reading a
+    //    whole token so that they agree on its amax without a barrier (the
+    //    same arithmetic as the router's quantisation: s = amax / 448, codes
+    //    E4M3(x / s)).  One token is split over waves 1-3, two tokens take
+    //    waves 2 and 3.
+    const bool from_x = a.x != nullptr;                 // M <= 2 only
     constexpr int NST = (MT * (H / 8) + 255) / 256;
     const int n8 = M * (H / 8);
     u32x2 stg[NST];
@@ -367,11 +369,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 #pragma unroll
         for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
         s_tok = a.act_s[min((int)threadIdx.x, M - 1)];
-    } else if (wave != 0) {
-        constexpr int NC8 = H / 8, CPL8 = (NC8 + kWave - 1) / kWave;   // 16-byte chunks of the token
+    } else if (wave >= M) {
+        constexpr int NC8 = H / 8, CPL8 = (NC8 + kWave - 1) / kWave;   // 16-byte chunks of a token
+        const int qw = wave - M, t = qw % M, split = (4 - M) / M, part = qw / M;
         u32x4 xv[CPL8];
 #pragma unroll
-        for (int i = 0; i < CPL8; ++i) xv[i] = reinterpret_cast<const u32x4*>(a.x)[min(lane + kWave * i, NC8 - 1)];
+        for (int i = 0; i < CPL8; ++i)
+            xv[i] = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H)[min(lane + kWave * i, NC8 - 1)];
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL8; ++i)
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 #pragma unroll
         for (int i = 0; i < CPL8; ++i) {
             const int c = lane + kWave * i;
-            if (c < NC8 && i % 3 == wave - 1) {
+            if (c < NC8 && i % split == part) {
                 const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
                 uint32_t code[2] = {0u, 0u};
 #pragma unroll
@@ -389,10 +393,10 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
                     const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
                     code[j >> 2] |= e4m3_encode(__uint_as_float(b) / s) << (8 * (j & 3));
                 }
-                act[(c & 3) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
+                act[(t * 4 + (c & 3)) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
             }
         }
-        if (wave == 1 && lane == 0) act_sl[0] = s;
+        if (part == 0 && lane == 0) act_sl[t] = s;
     }
     // 1. routing, derived independently by every workgroup (the staging loads
     //    above are in flight meanwhile); workgroup 0 publishes it for the down

@@ -331,11 +331,11 @@ moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hid
         if ((st = enqueue_sort(shape, M, ids, c, s, has_shared(sh))) != MOE_OK) return st;
         return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2), sh);
     }
-    // One token: the gate/up kernel quantises the activations itself (its
-    // idle waves do it during the routing prologue), so the router only
-    // computes logits.  More tokens: the router quantises them, a slice per
-    // workgroup.
-    const bool one = M == 1;
+    // One or two tokens: the gate/up kernel quantises the activations itself
+    // (its waves that derive no routing do it during the routing prologue),
+    // so the router only computes logits.  More tokens: the router quantises
+    // them, a slice per workgroup.
+    const bool one = M <= 2;
     if ((st = enqueue_router(shape, M, hidden, router_w, one ? nullptr : q, one ? nullptr : sc, c, s, ev(0))) !=
         MOE_OK)
         return st;

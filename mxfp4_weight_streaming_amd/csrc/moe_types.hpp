@@ -79,7 +79,7 @@ struct GateUpArgs {
     const float* act_s;    // [M]
     float* h;              // [M*K (+M),I]
     SharedWeights sh;      // read when the compaction holds the shared slot
-    const uint16_t* x;     // [1,H] bf16, or nullptr.  When set (one token), the
+    const uint16_t* x;     // [M,H] bf16, or nullptr.  When set (M <= 2), the
                            // kernel quantises x itself and act_q/act_s are unused
 };
 

@@ -414,56 +414,56 @@ def test_deterministic_repeat(moe, ling_weights):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def _one_token_pair(moe, shp, li, dw, ws, shared=None):
-    """The fused one-token forward, and the staged path on the same inputs:
-    moe_route (its quantisation taps, ids and weights), then
-    moe_experts_forward."""
-    H, K = shp.hidden, shp.topk
+def _fused_and_staged(moe, shp, li, dw, ws, shared=None):
+    """The fused forward, and the staged path on the same inputs: moe_route
+    (its quantisation taps, ids and weights), then moe_experts_forward."""
+    M, H, K = li.M, shp.hidden, shp.topk
     x = dev(li.x)
-    out_f = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    out_f = torch.empty((M, H), dtype=torch.float32, device="cuda")
     if shared is None:
-        moe.moe_decode_forward(shp, 1, x, dw.wr, dw.w13, dw.s13, dw.w2, dw.s2, out_f, ws)
+        moe.moe_decode_forward(shp, M, x, dw.wr, dw.w13, dw.s13, dw.w2, dw.s2, out_f, ws)
     else:
-        moe.moe_decode_forward_shared(shp, 1, x, dw.wr, dw.w13, dw.s13, dw.w2, dw.s2, shared, out_f, ws)
-    ids = torch.empty((1, K), dtype=torch.int32, device="cuda")
-    w = torch.empty((1, K), dtype=torch.float32, device="cuda")
-    q = torch.empty((1, H), dtype=torch.uint8, device="cuda")
-    s = torch.empty(1, dtype=torch.float32, device="cuda")
-    moe.moe_route(shp, 1, x, dw.wr, ids, w, ws, taps={"act_fp8": q, "act_scale": s})
-    out_s = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        moe.moe_decode_forward_shared(shp, M, x, dw.wr, dw.w13, dw.s13, dw.w2, dw.s2, shared, out_f, ws)
+    ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    q = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    moe.moe_route(shp, M, x, dw.wr, ids, w, ws, taps={"act_fp8": q, "act_scale": s})
+    out_s = torch.empty((M, H), dtype=torch.float32, device="cuda")
     if shared is None:
-        moe.moe_experts_forward(shp, 1, q, s, ids, w, dw.w13, dw.s13, dw.w2, dw.s2, out_s, ws)
+        moe.moe_experts_forward(shp, M, q, s, ids, w, dw.w13, dw.s13, dw.w2, dw.s2, out_s, ws)
     else:
-        moe.moe_experts_forward_shared(shp, 1, q, s, ids, w, dw.w13, dw.s13, dw.w2, dw.s2, shared, out_s, ws)
+        moe.moe_experts_forward_shared(shp, M, q, s, ids, w, dw.w13, dw.s13, dw.w2, dw.s2, shared, out_s, ws)
     torch.cuda.synchronize()
     return host(out_f), host(out_s), host(q), host(s)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_one_token_forward_equals_staged_path(moe, ling_weights, seed):
-    """At one token the gate/up kernel quantises the activations itself (the
-    router then computes logits only).  The layer output must equal, bit for
-    bit, the staged path whose codes come from the router's quantisation, and
-    those codes are bit-exact with the oracle (P1)."""
+@pytest.mark.parametrize("M,seed", [(1, 0), (1, 1), (1, 2), (2, 3), (2, 4)])
+def test_small_forward_equals_staged_path(moe, ling_weights, M, seed):
+    """At one or two tokens the gate/up kernel quantises the activations
+    itself (the router then computes logits only).  The layer output must
+    equal, bit for bit, the staged path whose codes come from the router's
+    quantisation, and those codes are bit-exact with the oracle (P1)."""
     w, dw = ling_weights
-    li = synth.decode_tokens(300 + seed, w, 1, K=8)
+    li = synth.decode_tokens(300 + seed, w, M, K=8)
     shp = _shape(moe, w, 8)
     ws = _ws(moe, shp)
-    fused, staged, q, s = _one_token_pair(moe, shp, li, dw, ws)
+    fused, staged, q, s = _fused_and_staged(moe, shp, li, dw, ws)
     assert np.array_equal(fused.view(np.uint32), staged.view(np.uint32))
     rq, rs = oracle.quant_act(li.x)
     assert np.array_equal(q, rq) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
 
 
-def test_one_token_forward_equals_staged_path_tiny_shared(moe):
-    """The same at the tiny shape, where one wave quantises the whole token,
-    without and with a shared expert."""
+@pytest.mark.parametrize("M", [1, 2])
+def test_small_forward_equals_staged_path_tiny_shared(moe, M):
+    """The same at the tiny shape (one wave quantises a whole token), without
+    and with a shared expert."""
     w = synth.expert_weights(71, 256, 64, 16)
-    li = synth.decode_tokens(72, w, 1, K=2)
+    li = synth.decode_tokens(72 + M, w, M, K=2)
     shp = _shape(moe, w, 2)
     dw, ws = DevWeights(w), _ws(moe, shp)
-    fused, staged, _, _ = _one_token_pair(moe, shp, li, dw, ws)
+    fused, staged, _, _ = _fused_and_staged(moe, shp, li, dw, ws)
     assert np.array_equal(fused.view(np.uint32), staged.view(np.uint32))
     sh = [dev(t) for t in synth.shared_expert(73, 256, 64)]
-    fused, staged, _, _ = _one_token_pair(moe, shp, li, dw, ws, shared=sh)
+    fused, staged, _, _ = _fused_and_staged(moe, shp, li, dw, ws, shared=sh)
     assert np.array_equal(fused.view(np.uint32), staged.view(np.uint32))
