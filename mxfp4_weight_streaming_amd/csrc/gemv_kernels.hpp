@@ -608,20 +608,24 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a)
 
 // ---------------------------------------------------------------------------
 // Down GEMV + combine.  A workgroup owns RPB output rows for every token; its
-// 8 waves split the selected experts (wave w takes slots w, w+8, ...), each
-// accumulating per-token partial sums in a fixed slot order; the waves' sums
-// are then added in wave order.  The FP8 intermediate of every pair is held
+// 8 waves split the selected experts (wave w takes slots w, w+8, ...).  Each
+// lane accumulates, per token, its share of the row's dot products over the
+// wave's slots in slot order; the lanes' sums are then added in a fixed order
+// (waves, then the row's lanes).  The FP8 intermediate of every pair is held
 // once per workgroup as f16 in LDS.
 // ---------------------------------------------------------------------------
 template <int H, int I>
 struct DownGeom {
     static constexpr int kChunks = I / 32;
-    static constexpr int kLanesPerRow = down_lanes_per_row(I);
-    static constexpr int kChunksPerLane = kChunks / kLanesPerRow;
-    static constexpr int kRowsPerBlock = kWave / kLanesPerRow;
-    static_assert(kRowsPerBlock == down_rows_per_block(I), "down blocking");
+    static constexpr int kRowsPerBlock = down_rows_per_block(H, I);
+    static constexpr int kPasses = down_row_passes(H, I);
+    static constexpr int kRowsPerPass = kRowsPerBlock / kPasses;
+    static constexpr int kLanesPerRow = down_lanes_per_row(H, I);
+    static constexpr int kChunksPerLane = kChunks / kLanesPerRow;   // per pass
+    static constexpr int kLanesUsed = kRowsPerPass * kLanesPerRow;
     static constexpr int kWaves = 8;
-    static_assert(I % 32 == 0 && H % kRowsPerBlock == 0, "unsupported down shape");
+    static_assert(I % 32 == 0 && kChunks % kLanesPerRow == 0 && kLanesUsed <= kWave && H % kRowsPerBlock == 0 &&
+                  kRowsPerBlock % kPasses == 0, "unsupported down shape");
 };
 
 template <int H, int I, int MT, bool FROM_H>
@@ -629,8 +633,8 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
 {
     using G = DownGeom<H, I>;
     constexpr int CH = G::kChunks, LPR = G::kLanesPerRow, CPL = G::kChunksPerLane, RPB = G::kRowsPerBlock;
-    extern __shared__ u32x4 q2h[];                 // [pair][q][chunk] of 8 halves
-    __shared__ float red[G::kWaves][RPB][MT];
+    constexpr int RP = G::kPasses, RPW = G::kRowsPerPass, NW = RP * CPL;   // NW blocks of 32 per lane and slot
+    extern __shared__ u32x4 q2h[];    // [pair][q][chunk] of 8 halves; at the end [wave][token][pass][lane] sums
     __shared__ float s2l[kMaxPairsExt];
     __shared__ int32_t c_exp[kMaxPairs + 1], c_off[kMaxPairs + 2], c_src[kMaxPairsExt], c_tok[kMaxPairsExt];
     __shared__ float c_w[kMaxPairsExt];            // router weight of each pair (1 for the shared expert's rows)
@@ -642,7 +646,9 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     // scalar load: its waits then never hold up the vector loads of h and of
     // the weights, which are counted separately
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int li = lane % LPR, grp = lane / LPR;
+    // this lane's row in pass h is n + h * RPW; lanes past RPW * LPR repeat
+    // the last row's loads, and their sums are unused
+    const int li = lane % LPR, grp = min(lane / LPR, RPW - 1);
     const int n = blockIdx.x * RPB + grp;
 
     // The compaction, copied to LDS once: its loads go out first, so waiting
@@ -657,7 +663,8 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     const int32_t ct = a.cp.pair_token[min(tid, Pe - 1)];
     const float cw = a.topk_w[min(tid, P - 1)];
     const int last = max(n_act - 1, 0);
-    // a slot's loads: a wave-uniform expert base plus this lane's fixed offset
+    // a slot's loads: a wave-uniform expert base plus this lane's fixed
+    // offsets; block j = h * CPL + i is chunk li + LPR i of the pass-h row
     const uint32_t woff = (uint32_t)n * (I / 2) + (uint32_t)li * 16, soff = (uint32_t)n * CH + (uint32_t)li;
     auto load_slot = [&](int ea_any, u32x4* wv, uint32_t* sv) {
         const int ea = __builtin_amdgcn_readfirstlane(ea_any);
@@ -666,9 +673,15 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
         const uint8_t* wb = sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
         const uint8_t* sb = sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) wv[i] = load_stream(reinterpret_cast<const u32x4*>(wb + woff + LPR * 16 * i));
+        for (int h = 0; h < RP; ++h)
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) sv[i] = sb[soff + LPR * i];
+            for (int i = 0; i < CPL; ++i)
+                wv[h * CPL + i] = load_stream(
+                    reinterpret_cast<const u32x4*>(wb + woff + (uint32_t)(h * RPW) * (I / 2) + LPR * 16 * i));
+#pragma unroll
+        for (int h = 0; h < RP; ++h)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[soff + (uint32_t)(h * RPW) * CH + LPR * i];
     };
 
     // The intermediate in LDS as f16.  From h: a wave per (token, expert) row
@@ -684,8 +697,8 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     }
     // two weight buffers used in turn (no register copies, which would wait
     // for loads in flight): A holds this wave's first slot from here on
-    u32x4 wA[CPL], wB[CPL];
-    uint32_t sA[CPL], sB[CPL];
+    u32x4 wA[NW], wB[NW];
+    uint32_t sA[NW], sB[NW];
     load_slot(a.cp.act_experts[min(wave, last)], wA, sA);   // a scalar load of the expert id
     if (tid < nc) c_exp[tid] = ce;
     if (tid <= nc) c_off[tid] = co;
@@ -759,35 +772,44 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     }
     __syncthreads();
 
-    float acc[MT];
+    float acc[RP][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+    for (int h = 0; h < RP; ++h)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[h][t] = 0.0f;
     auto consume = [&](int slot, const u32x4* wv, const uint32_t* sv) {
-        half2_t hw[CPL * 16];
+        half2_t hw[NW * 16];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            e2m1x8_to_half(wv[i].x, hw + 16 * i + 0);
-            e2m1x8_to_half(wv[i].y, hw + 16 * i + 4);
-            e2m1x8_to_half(wv[i].z, hw + 16 * i + 8);
-            e2m1x8_to_half(wv[i].w, hw + 16 * i + 12);
+        for (int j = 0; j < NW; ++j) {
+            e2m1x8_to_half(wv[j].x, hw + 16 * j + 0);
+            e2m1x8_to_half(wv[j].y, hw + 16 * j + 4);
+            e2m1x8_to_half(wv[j].z, hw + 16 * j + 8);
+            e2m1x8_to_half(wv[j].w, hw + 16 * j + 12);
         }
         const int q0 = min(max(c_off[slot], 0), Pe), q1 = min(c_off[slot + 1], Pe);
         for (int qq = q0; qq < q1; ++qq) {
             const int p = min(max(c_src[qq], 0), Pe - 1);
             const int tok = c_tok[qq];
-            float d = 0.0f;
+            float d[RP];
+#pragma unroll
+            for (int h = 0; h < RP; ++h) d[h] = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
+                // the pair's chunk c serves this lane's row of every pass
                 const int c = li + LPR * i;
                 const u32x4 a0 = q2h[(p * 4 + 0) * CH + c], a1 = q2h[(p * 4 + 1) * CH + c];
                 const u32x4 a2 = q2h[(p * 4 + 2) * CH + c], a3 = q2h[(p * 4 + 3) * CH + c];
-                d += ldexp_e8m0(block_dot(hw + 16 * i, a0, a1, a2, a3), sv[i]);
+#pragma unroll
+                for (int h = 0; h < RP; ++h)
+                    d[h] += ldexp_e8m0(block_dot(hw + 16 * (h * CPL + i), a0, a1, a2, a3), sv[h * CPL + i]);
             }
-            d = group_sum<LPR>(d);
             const float coef = c_w[p] * s2l[p];
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                if (t == tok) acc[t] = fmaf(coef, d, acc[t]);
+            for (int t = 0; t < MT; ++t) {
+                const float ct = (t == tok) ? coef : 0.0f;    // a select, not an indexed store
+#pragma unroll
+                for (int h = 0; h < RP; ++h) acc[h][t] = fmaf(ct, d[h], acc[h][t]);
+            }
         }
     };
     // slots wave, wave + 8, ...: the next slot's weights load while this one
@@ -808,16 +830,23 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
             consume(slot, wB, sB);
         }
     }
-    if (li == 0) {
+    // the lanes' sums go to the intermediate's LDS once every wave is past
+    // its last read of it
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(q2h);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) red[wave][grp][t] = acc[t];
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int h = 0; h < RP; ++h) red[((wave * MT + t) * RP + h) * kWave + lane] = acc[h][t];
     __syncthreads();
     for (int idx = threadIdx.x; idx < RPB * a.M; idx += blockDim.x) {
         const int row = idx % RPB, t = idx / RPB;
-        float s = red[0][row][t];
+        const int h = row / RPW, rr = row % RPW;
+        float s = 0.0f;
+        for (int w = 0; w < G::kWaves; ++w) {
 #pragma unroll
-        for (int w = 1; w < G::kWaves; ++w) s += red[w][row][t];
+            for (int j = 0; j < LPR; ++j) s += red[((w * MT + t) * RP + h) * kWave + rr * LPR + j];
+        }
         a.out[(size_t)t * H + blockIdx.x * RPB + row] = s;
     }
 }

@@ -345,7 +345,7 @@ JitStatus get_entry(int H, int I, const char* arch, const char* cache_dir, Entry
         snprintf(b, sizeof b,
                  "(H=%d, I=%d) has no kernel geometry: needs 256 <= H <= 8192, 64 <= I <= 4096, H %% 32 == 0, "
                  "I %% 64 == 0, I %% %d == 0 and H %% %d == 0",
-                 H, I, gate_up_rows_per_block(H), down_rows_per_block(I));
+                 H, I, gate_up_rows_per_block(H), down_rows_per_block(H, I));
         *err = b;
         return JitStatus::BadShape;
     }

@@ -72,13 +72,15 @@ hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, c
     if (a.sh.w2 != nullptr && a.h == nullptr) return hipErrorInvalidValue;
     const Kern k = find_kernel(key_down(H, I, mt, a.h != nullptr));
     if (!k.ok()) return hipErrorInvalidDeviceFunction;
-    const size_t lds = (size_t)(a.M * a.K + (a.sh.w2 != nullptr ? a.M : 0)) * I * 2;
+    // the intermediate as f16, and afterwards the lanes' sums (8 waves x mt tokens x row passes x 64 lanes)
+    const size_t lds = std::max((size_t)(a.M * a.K + (a.sh.w2 != nullptr ? a.M : 0)) * I * 2,
+                                (size_t)8 * mt * down_row_passes(H, I) * kWaveSize * sizeof(float));
     if (lds > kMaxDynamicLds) return hipErrorInvalidValue;
     if (lds > 64 * 1024 && k.aot != nullptr) {   // above the default dynamic-LDS limit of a compiled kernel
         hipError_t err = hipFuncSetAttribute(k.aot, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
     }
-    return launch_kern(k, dim3(H / down_rows_per_block(I)), dim3(512), (uint32_t)lds, s, ev, a);
+    return launch_kern(k, dim3(H / down_rows_per_block(H, I)), dim3(512), (uint32_t)lds, s, ev, a);
 }
 
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s)
@@ -109,13 +111,13 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s)
 void kernel_names(int H, int I, char* buf, size_t n)
 {
     const Kern k = find_kernel(key_gate_up(H, I, 1));
-    const int lg = gate_up_lanes_per_row(H), ld = down_lanes_per_row(I);
+    const int lg = gate_up_lanes_per_row(H), ld = down_lanes_per_row(H, I);
     snprintf(buf, n,
              "router_kernel<H=%d> -> gate_up_kernel<H=%d,I=%d> (routing prologue; %d lanes/row, %d row-pairs per "
              "item, %d items/expert, up to 512 WGs) -> down_kernel<H=%d,I=%d> (FP8 requantisation prologue; %d "
-             "lanes/row, %d rows/WG, %d WGs)%s",
-             H, H, I, lg, gate_up_rows_per_block(H), I / gate_up_rows_per_block(H), H, I, ld, down_rows_per_block(I),
-             H / down_rows_per_block(I), k.jit != nullptr ? " [compiled at run time]" : "");
+             "lanes/row, %d rows/WG in %d passes, %d WGs)%s",
+             H, H, I, lg, gate_up_rows_per_block(H), I / gate_up_rows_per_block(H), H, I, ld, down_rows_per_block(H, I),
+             down_row_passes(H, I), H / down_rows_per_block(H, I), k.jit != nullptr ? " [compiled at run time]" : "");
 }
 
 }  // namespace moe

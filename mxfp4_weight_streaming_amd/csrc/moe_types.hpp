@@ -193,19 +193,61 @@ __host__ __device__ constexpr int gate_up_lanes_per_row(int H)
 }
 __host__ __device__ constexpr int gate_up_rows_per_block(int H) { return (kWaveSize / gate_up_lanes_per_row(H)) * 4; }
 
-// down GEMV: I/32 chunks per row, LPR lanes per row, one row per LPR lanes.
-__host__ __device__ constexpr int down_lanes_per_row(int I)
+// down GEMV: a workgroup owns RPB output rows.  A wave covers those rows of
+// one expert in RP passes of RPW = RPB / RP rows, LPR lanes per row (each lane
+// holds I/32/LPR of a row's 32-element blocks per pass), so that one load
+// instruction reads LPR * 16 contiguous bytes of each of RPW rows.  The
+// workgroups are all resident at once (8 waves each), so the grid H / RPB is
+// kept at or below the chip's 256 compute units where the shape allows: a
+// grid above it puts two workgroups on some compute units, and those finish
+// last.  RPB is the smallest divisor of H giving such a grid for which some
+// RP (the smallest) has LPR a multiple of 4 (whole 64-byte pieces per
+// instruction, or the whole row), at most 4 blocks per lane and at least half
+// the wave busy.  Other shapes take one pass of 64 / LPR rows with the
+// largest power-of-two LPR (up to 8) dividing I/32.
+constexpr int kComputeUnits = 256;
+constexpr int kDownMaxBlocksPerLane = 4;
+__host__ __device__ constexpr int down_lanes_for_rows(int I, int rpw)
 {
-    return ((I / 32) % 8 == 0) ? 8 : ((I / 32) % 4 == 0) ? 4 : ((I / 32) % 2 == 0) ? 2 : 1;
+    int l = kWaveSize / rpw;
+    while (l > 1 && (I / 32) % l != 0) --l;
+    return l;
 }
-__host__ __device__ constexpr int down_rows_per_block(int I) { return kWaveSize / down_lanes_per_row(I); }
+__host__ __device__ constexpr bool down_blocking_ok(int I, int rpb, int rp)
+{
+    if (rpb % rp != 0 || rpb / rp > kWaveSize) return false;
+    const int rpw = rpb / rp, l = down_lanes_for_rows(I, rpw), c = I / 32;
+    return (c / l) * rp <= kDownMaxBlocksPerLane && 2 * l * rpw >= kWaveSize && (l % 4 == 0 || l == c);
+}
+constexpr int kDownMaxPasses = 4;
+__host__ __device__ constexpr int down_rows_per_block(int H, int I)
+{
+    for (int r = (H + kComputeUnits - 1) / kComputeUnits; r <= kWaveSize * kDownMaxPasses; ++r) {
+        if (H % r != 0) continue;
+        for (int rp = 1; rp <= kDownMaxPasses; ++rp)
+            if (down_blocking_ok(I, r, rp)) return r;
+    }
+    const int c = I / 32;
+    return kWaveSize / ((c % 8 == 0) ? 8 : (c % 4 == 0) ? 4 : (c % 2 == 0) ? 2 : 1);
+}
+__host__ __device__ constexpr int down_row_passes(int H, int I)
+{
+    const int r = down_rows_per_block(H, I);
+    for (int rp = 1; rp <= kDownMaxPasses; ++rp)
+        if (down_blocking_ok(I, r, rp)) return rp;
+    return 1;
+}
+__host__ __device__ constexpr int down_lanes_per_row(int H, int I)
+{
+    return down_lanes_for_rows(I, down_rows_per_block(H, I) / down_row_passes(H, I));
+}
 
 // The decode (GEMV) path's kernels exist for (H, I) when these hold (the
 // kernels' own static checks repeat them).
 __host__ __device__ constexpr bool gemv_shape_ok(int H, int I)
 {
     return H >= 256 && H <= 8192 && H % 32 == 0 && I >= 64 && I <= 4096 && I % kWaveSize == 0 &&
-           I % gate_up_rows_per_block(H) == 0 && H % down_rows_per_block(I) == 0;
+           I % gate_up_rows_per_block(H) == 0 && H % down_rows_per_block(H, I) == 0;
 }
 
 // Chunk path blocking: 16-row MFMA tiles, 64-row chunks, 32 gate/up rows and
