@@ -207,6 +207,55 @@ __device__ void publish_route(const RouteLds& r, const RouteSrc& src, int32_t* i
     if (tid == 0) *cp.n_act = r.n_act;
 }
 
+// One token routed from its logits, in the gate/up kernel.  The workgroup's
+// slots are ranks: slot s < K is the rank-s expert with pair s (token 0), and
+// slot K the shared expert with pair K.  The weights of a slot are needed
+// before the rest of the routing, so wave 0 ranks only up to the workgroup's
+// own slot (slot_me) and the loads go out as soon as that expert is known;
+// workgroup 0 ranks all K and publishes the routing and the ascending-id
+// compaction that route_prologue and publish_route would give.
+__device__ void route_rank1(const RouteSrc& src, int slot_me, RouteLds& r, int32_t* ids_out, float* w_out,
+                            const Compaction& cp)
+{
+    const int tid = threadIdx.x, K = src.K;
+    const int R = blockIdx.x == 0 ? K : min(slot_me + 1, K);
+    if ((tid >> 6) == 0) topk_wave(src.logits, src.E, K, r.ids, r.w, R);
+    __syncthreads();
+    const int n = K + (src.shared ? 1 : 0);
+    if (tid <= K) {
+        r.act_experts[tid] = tid < K ? r.ids[min(tid, R - 1)] : kSharedExpert;
+        r.offsets[tid] = tid;
+        r.pair_token[tid] = 0;
+        r.pair_src[tid] = tid;
+    }
+    if (tid == 0) {
+        r.n_act = n;
+        r.offsets[n] = n;
+    }
+    if (blockIdx.x != 0) return;
+    if (tid < K) {
+        const int e = r.ids[tid];
+        int s = 0;
+        for (int q = 0; q < K; ++q) s += r.ids[q] < e ? 1 : 0;   // the K experts are distinct
+        cp.act_experts[s] = e;
+        cp.offsets[s] = s;
+        cp.pair_token[s] = 0;
+        cp.pair_src[s] = tid;
+        if (ids_out != nullptr) ids_out[tid] = e;
+        if (w_out != nullptr) w_out[tid] = r.w[tid];
+    }
+    if (tid == 0) {
+        if (src.shared) {
+            cp.act_experts[K] = kSharedExpert;
+            cp.pair_token[K] = 0;
+            cp.pair_src[K] = K;
+        }
+        cp.offsets[K] = K;
+        cp.offsets[n] = n;
+        *cp.n_act = n;
+    }
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a)
 {
     __shared__ RouteLds r;
@@ -400,9 +449,14 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     }
     // 1. routing, derived independently by every workgroup (the staging loads
     //    above are in flight meanwhile); workgroup 0 publishes it for the down
-    //    kernel (and the caller)
-    route_prologue(a.src, rl);
-    if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
+    //    kernel (and the caller).  One token routed from its logits: slots are
+    //    ranks, and a workgroup ranks only up to its own slot (route_rank1).
+    if (MT == 1 && a.src.logits != nullptr) {
+        route_rank1(a.src, min((int)blockIdx.x / BPE, a.src.K), rl, a.ids_out, a.w_out, a.cp);
+    } else {
+        route_prologue(a.src, rl);
+        if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
+    }
     if (!from_x) {
 #pragma unroll
         for (int j = 0; j < NST; ++j) {
@@ -496,7 +550,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     issue(blockIdx.x, st[0]);
     if constexpr (IPW <= 4) {
         // Unrolled over IPW items, with the look-ahead unconditional (past the
-        // last item, this item's rows again, unused): the two stages are never
+        // last item, this item's rows again, unused; none from the IPW-th item,
+        // whose successor the loop below loads itself): the two stages are never
         // carried around a loop edge (register copies there would wait for
         // the loads in flight) and each wait covers exactly the item in use.
 #pragma unroll
@@ -504,7 +559,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             const int cur = blockIdx.x + k * gridDim.x;
             if (cur >= n_items) break;
             const int nxt = cur + gridDim.x;
-            issue(nxt < n_items ? nxt : cur, st[(k + 1) & 1]);
+            if (k + 1 < IPW) issue(nxt < n_items ? nxt : cur, st[(k + 1) & 1]);
             compute(cur, st[k & 1]);
         }
         // beyond IPW items (not reached with the launch geometry): one at a time

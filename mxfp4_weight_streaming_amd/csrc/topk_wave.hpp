@@ -49,7 +49,7 @@ __device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b
 }
 
 template <int PER>
-__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out)
+__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out, int R)
 {
     const int lane = threadIdx.x & 63;
     uint32_t u[PER];
@@ -79,7 +79,7 @@ __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, floa
     uint32_t my_u = 0u;                         // lane r ends with the rank-r value and expert
     int my_e = 0;
     uint32_t top = 0u;
-    for (int r = 0; r < K; ++r) {
+    for (int r = 0; r < R; ++r) {
         const uint32_t m = wave_max_u32(u[0]);
         const uint64_t b = __ballot(u[0] == m);
         int wl = (int)__builtin_ctzll(b);
@@ -103,6 +103,10 @@ __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, floa
             s[PER - 1] = PER;
         }
     }
+    if (R < K) {                                // the first R ranks only: their experts
+        if (lane < R) ids_out[lane] = my_e;
+        return;
+    }
     const float lmax = f32_from_orderable(top);
     const float ex = (lane < K) ? expf(f32_from_orderable(my_u) - lmax) : 0.0f;
     const float den = wave_sum(ex);
@@ -112,12 +116,17 @@ __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, floa
     }
 }
 
-__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out)
+// Top-K of one token's E logits by one wave: ids_out[r] is the rank-r expert
+// and w_out[r] its softmax weight over the K selected.  With R < K only the
+// first R ranks are found (ids only; their ranking is the same as in the
+// full call).
+__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out, int R = -1)
 {
-    if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out);
-    else if (E <= 128) topk_wave_t<2>(L, E, K, ids_out, w_out);
-    else if (E <= 256) topk_wave_t<4>(L, E, K, ids_out, w_out);
-    else topk_wave_t<8>(L, E, K, ids_out, w_out);
+    if (R < 0 || R > K) R = K;
+    if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out, R);
+    else if (E <= 128) topk_wave_t<2>(L, E, K, ids_out, w_out, R);
+    else if (E <= 256) topk_wave_t<4>(L, E, K, ids_out, w_out, R);
+    else topk_wave_t<8>(L, E, K, ids_out, w_out, R);
 }
 
 }  // namespace moe
