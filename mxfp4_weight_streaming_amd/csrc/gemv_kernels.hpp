@@ -472,10 +472,18 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     const int n_items = rl.n_act * BPE;
 
     // 2. work items (selected expert, block of rows), strided over the grid;
-    //    the next item's weight loads are in flight while this one computes
+    //    the next item's weight loads are in flight while this one computes.
+    //    A row's CH block scales are contiguous bytes.  When LPR and CH are
+    //    multiples of 4, the row's LPR lanes load them as dwords (lane li:
+    //    dwords li, li + LPR, ...), and the lane that uses block li + LPR i
+    //    takes that byte from the lane holding its dword, in dword register
+    //    i / 4 (a cross-lane read): NSW dword loads per row instead of CPL
+    //    byte loads.  Otherwise each lane loads its CPL scale bytes.
+    constexpr bool kScaleDw = LPR % 4 == 0 && CH % 4 == 0;
+    constexpr int NSW = kScaleDw ? (CH / 4 + LPR - 1) / LPR : CPL;
     struct Stage {
         u32x4 wg[CPL], wu[CPL];
-        uint32_t sg[CPL], su[CPL];
+        uint32_t sg[NSW], su[NSW];
     };
     auto issue = [&](int item, Stage& st) {
         const int slot = item / BPE, rb = item % BPE;
@@ -493,10 +501,29 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             st.wg[i] = load_stream(grow + li + LPR * i);
             st.wu[i] = load_stream(urow + li + LPR * i);
         }
+        if constexpr (kScaleDw) {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            st.sg[i] = gsc[li + LPR * i];
-            st.su[i] = usc[li + LPR * i];
+            for (int j = 0; j < NSW; ++j) {
+                const int d = min(li + LPR * j, CH / 4 - 1);       // past the row's end: its last dword again
+                st.sg[j] = reinterpret_cast<const uint32_t*>(gsc)[d];
+                st.su[j] = reinterpret_cast<const uint32_t*>(usc)[d];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                st.sg[i] = gsc[li + LPR * i];
+                st.su[i] = usc[li + LPR * i];
+            }
+        }
+    };
+    // the scale code of block li + LPR i of this lane's row
+    auto scale_of = [&](const uint32_t* sw, int i) -> uint32_t {
+        if constexpr (kScaleDw) {
+            const int src = LPR * grp + ((LPR / 4) * i + li / 4) % LPR;
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)sw[i / 4]);
+            return (v >> (8 * (li & 3))) & 0xFFu;
+        } else {
+            return sw[i];
         }
     };
     auto compute = [&](int item, Stage& st) {
@@ -507,6 +534,12 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
         float accg[MT], accu[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) accg[t] = accu[t] = 0.0f;
+        uint32_t scg[CPL], scu[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            scg[i] = scale_of(st.sg, i);
+            scu[i] = scale_of(st.su, i);
+        }
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = li + LPR * i;
@@ -525,8 +558,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
                     const int tok = rl.pair_token[p0 + t];
                     const u32x4 a0 = act[(tok * 4 + 0) * CH + c], a1 = act[(tok * 4 + 1) * CH + c];
                     const u32x4 a2 = act[(tok * 4 + 2) * CH + c], a3 = act[(tok * 4 + 3) * CH + c];
-                    accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), st.sg[i]);
-                    accu[t] += ldexp_e8m0(block_dot(hu, a0, a1, a2, a3), st.su[i]);
+                    accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), scg[i]);
+                    accu[t] += ldexp_e8m0(block_dot(hu, a0, a1, a2, a3), scu[i]);
                 }
             }
         }
