@@ -49,16 +49,23 @@ __device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b
 }
 
 template <int PER>
-__device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, float* w_out, int R)
+__device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t* ids_out, float* w_out, int R)
 {
     const int lane = threadIdx.x & 63;
+    // the logits are in global memory: loads through a global pointer are
+    // counted by one counter and waited for together (a generic pointer gives
+    // flat loads, counted by two)
+    const __attribute__((address_space(1))) float* L = (const __attribute__((address_space(1))) float*)Lg;
     uint32_t u[PER];
     int s[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {             // unconditional loads: all in flight together
         const int e = lane + kWave * i;
         const float v = L[e < E ? e : E - 1];
-        u[i] = (e < E) ? f32_orderable(v + 0.0f) : 0u;   // + 0.0f folds -0 into +0; 0 is below every key
+        // + 0.0f folds -0 into +0; 0 is below every key.  The mask is
+        // arithmetic, so the load's result is always used and the compiler
+        // cannot move the load into a branch (with a wait of its own)
+        u[i] = f32_orderable(v + 0.0f) & (0u - (uint32_t)(e < E));
         s[i] = i;
     }
     // sorting network over the lane's entries (a strict order: slots differ)
@@ -120,7 +127,7 @@ __device__ void topk_wave_t(const float* L, int E, int K, int32_t* ids_out, floa
 // and w_out[r] its softmax weight over the K selected.  With R < K only the
 // first R ranks are found (ids only; their ranking is the same as in the
 // full call).
-__device__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out, int R = -1)
+__device__ __forceinline__ void topk_wave(const float* L, int E, int K, int32_t* ids_out, float* w_out, int R = -1)
 {
     if (R < 0 || R > K) R = K;
     if (E <= 64) topk_wave_t<1>(L, E, K, ids_out, w_out, R);
