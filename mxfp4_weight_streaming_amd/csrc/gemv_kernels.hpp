@@ -753,7 +753,10 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     const int last = max(n_act - 1, 0);
     // a slot's loads: a wave-uniform expert base plus this lane's fixed
     // offsets; block j = h * CPL + i is chunk li + LPR i of the pass-h row
-    const uint32_t woff = (uint32_t)n * (I / 2) + (uint32_t)li * 16, soff = (uint32_t)n * CH + (uint32_t)li;
+    // (24-bit products: a 64-bit multiply-add here takes an unused high half
+    // from whatever register, which can be one a load in flight writes)
+    const uint32_t woff = __umul24((uint32_t)n, (uint32_t)(I / 2)) + (uint32_t)li * 16;
+    const uint32_t soff = __umul24((uint32_t)n, (uint32_t)CH) + (uint32_t)li;
     auto load_slot = [&](int ea_any, u32x4* wv, uint32_t* sv) {
         const int ea = __builtin_amdgcn_readfirstlane(ea_any);
         const bool sh = shared && ea == kSharedExpert;
@@ -770,6 +773,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
         for (int h = 0; h < RP; ++h)
 #pragma unroll
             for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[soff + (uint32_t)(h * RPW) * CH + LPR * i];
+        __builtin_amdgcn_sched_barrier(0);   // the slot's loads go out here, not next to their uses
     };
 
     // The intermediate in LDS as f16.  From h: a wave per (token, expert) row
