@@ -355,6 +355,21 @@ def test_layer_all_experts_selected(moe):
     _check_layer(moe, shp, li, DevWeights(w), _ws(moe, shp))
 
 
+@pytest.mark.parametrize("E,K", [(40, 4), (100, 8), (200, 8), (300, 8)])
+def test_route_and_layer_partial_logit_loads(moe, E, K):
+    """Expert counts that fill a lane's last logits load only in part (E % 64
+    != 0, one to eight logits per lane): the top-K masks the lanes past E.
+    Routing (P1, P2, compaction) and the whole layer (P5) at 1 token (gate/up
+    ranks in rank order) and 3 tokens (the compaction path)."""
+    w = synth.expert_weights(80 + E, 256, 64, E)
+    shp = _shape(moe, w, K)
+    dw = DevWeights(w)
+    for M in (1, 3):
+        li = synth.decode_tokens(81 + E + M, w, M, K=K)
+        _check_route(moe, shp, li, dw, _ws(moe, shp))
+        _check_layer(moe, shp, li, dw, _ws(moe, shp))
+
+
 def test_layer_zero_hidden(moe):
     w = synth.expert_weights(13, 256, 64, 16)
     x = synth.bf16_from_f32(np.zeros((2, 256), np.float32))
