@@ -791,7 +791,11 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     // for loads in flight): A holds this wave's first slot from here on
     u32x4 wA[NW], wB[NW];
     uint32_t sA[NW], sB[NW];
-    load_slot(a.cp.act_experts[min(wave, last)], wA, sA);   // a scalar load of the expert id
+    // the expert id by a scalar load, its index clamped by a bound from the
+    // arguments rather than by the count of active experts (one load fewer
+    // before the weights go out; past that count the id is stale but in
+    // range, and its slot is never used)
+    load_slot(a.cp.act_experts[min(wave, nc - 1)], wA, sA);
     if (tid < nc) c_exp[tid] = ce;
     if (tid <= nc) c_off[tid] = co;
     if (tid < Pe) {

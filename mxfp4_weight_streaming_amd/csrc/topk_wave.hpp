@@ -48,6 +48,9 @@ __device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b
     s[b] = sw ? sa : sb;
 }
 
+// One out-of-line body per logits-per-lane count, called through the inlined
+// dispatch below, where E is wave-uniform: every body inlined at every call
+// site made the gate/up kernels larger and slower.
 template <int PER>
 __device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t* ids_out, float* w_out, int R)
 {
