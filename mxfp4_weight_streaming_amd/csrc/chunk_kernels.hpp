@@ -398,15 +398,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const int ks0 = (has_k ? w : 0) * KQ;
     const int j0 = jq * kGuRows;
     const uint8_t* w13e = e == kSharedExpert ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
-    i32x8 bg[NJ][KQ], bu[NJ][KQ];
+    // The wave's K slice of a row is BPR 16-byte blocks (one E8M0 block each).
+    // Load i of lane l fetches block 64 i + l of an n-tile's 16 x BPR blocks in
+    // row-major order, so each row's slice arrives as one contiguous run (the
+    // operand layout itself would read 64 bytes from each of 16 rows per
+    // load, a slower pattern on HBM).  Group t < NJ is gate n-tile t, group
+    // NJ + t is up n-tile t.
+    constexpr int BPR = 4 * KQ, RSTR = BPR + 1;         // blocks per slice row; LDS row stride in blocks
+    __shared__ u32x4 xpose[4][16 * RSTR];               // per wave: one n-tile being rearranged
+    u32x4 raw[2 * NJ][KQ];
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-        const uint8_t* wg = w13e + (size_t)(j0 + 16 * nj + r) * (H / 2) + 16 * g;
-        const uint8_t* wu = wg + (size_t)I * (H / 2);
+    for (int t = 0; t < 2 * NJ; ++t) {
+        const uint8_t* nt = w13e + (size_t)((t < NJ ? 0 : I) + j0 + 16 * (t % NJ)) * (H / 2) + ks0 * 64;
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            bg[nj][q] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wg + (ks0 + q) * 64)));
-            bu[nj][q] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wu + (ks0 + q) * 64)));
+        for (int i = 0; i < KQ; ++i) {
+            const int b = i * 64 + lane;
+            raw[t][i] = load_stream(reinterpret_cast<const u32x4*>(nt + (size_t)(b / BPR) * (H / 2) + (b % BPR) * 16));
         }
     }
     int tok[kChunkTiles];
@@ -430,6 +437,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         s_row = a.act_s[t];
     };
     load_tile(tok[0]);
+    // into the operand layout through the wave's LDS area: lane (r, g) of
+    // k-step q takes block 4 q + g of row r (the row stride of BPR + 1 blocks
+    // keeps the 16 rows of one read on distinct banks)
+    i32x8 bg[NJ][KQ], bu[NJ][KQ];
+    u32x4* xw = xpose[w];
+#pragma unroll
+    for (int t = 0; t < 2 * NJ; ++t) {
+#pragma unroll
+        for (int i = 0; i < KQ; ++i) {
+            const int b = i * 64 + lane;
+            xw[(b / BPR) * RSTR + b % BPR] = raw[t][i];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            const i32x8 v = fp4_operand(xw[r * RSTR + 4 * q + g]);
+            if (t < NJ) bg[t][q] = v;
+            else bu[t - NJ][q] = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
     __syncthreads();                                     // block scales in LDS
     constexpr int NP = (KQ + 3) / 4;                    // packed scale registers per n-tile
     int sg[NJ][NP], su[NJ][NP];
@@ -521,20 +549,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const int n0 = nq * kDnRows;
     const uint8_t* w2e = e == kSharedExpert ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
     const uint8_t* sw2e = e == kSharedExpert ? a.sh.s2 : a.sw2 + (size_t)e * H * SROW;
-    i32x8 b[NJ][KS];
+    // A row is BPR 16-byte blocks (one E8M0 block each) and an n-tile's 16
+    // rows are one contiguous run of 16 BPR blocks: load i of lane l fetches
+    // block 64 i + l of it (the gate/up kernel's scheme; the operand layout
+    // would read 64 bytes from each of 16 rows per load).
+    constexpr int BPR = I / 32, NBLK = 16 * BPR, NLD = (NBLK + 63) / 64, RSTR = BPR + 1;
+    __shared__ u32x4 xpose[4][16 * RSTR];               // per wave: one n-tile being rearranged
+    u32x4 raw[NJ][NLD];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
-        const uint8_t* wrow = w2e + (size_t)(n0 + (w * NJ + nj) * 16 + r) * (I / 2);
+        const uint8_t* nt = w2e + (size_t)(n0 + (w * NJ + nj) * 16) * (I / 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int kb = ks * 128 + 32 * g;             // first K of this lane's block
-            if constexpr (I % 128 == 0) {
-                b[nj][ks] = fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wrow + kb / 2)));
-            } else {                                      // K padded with zero codes
-                const bool in = kb < I;
-                b[nj][ks] = in ? fp4_operand(load_stream(reinterpret_cast<const u32x4*>(wrow + (in ? kb / 2 : 0))))
-                               : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
+        for (int i = 0; i < NLD; ++i) {
+            const int b = i * 64 + lane;
+            raw[nj][i] = load_stream(reinterpret_cast<const u32x4*>(nt + (size_t)(b < NBLK ? b : NBLK - 1) * 16));
         }
     }
     if constexpr (SBYTES % 16 == 0) {
@@ -569,6 +597,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
     };
     load_tile(0);
+    // into the operand layout through the wave's LDS area: lane (r, g) of
+    // k-step ks takes block 4 ks + g of row r, zero codes past the row
+    i32x8 b[NJ][KS];
+    u32x4* xw = xpose[w];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int bi = i * 64 + lane;
+            if (NBLK % 64 == 0 || bi < NBLK) xw[(bi / BPR) * RSTR + bi % BPR] = raw[nj][i];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int blk = 4 * ks + g;
+            if constexpr (I % 128 == 0) {
+                b[nj][ks] = fp4_operand(xw[r * RSTR + blk]);
+            } else {                                      // K padded with zero codes
+                const u32x4 v = xw[r * RSTR + (blk < BPR ? blk : 0)];
+                b[nj][ks] = blk < BPR ? fp4_operand(v) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
     __syncthreads();                                      // block scales in LDS
     constexpr int NP = (KS + 3) / 4;                    // packed scale registers per n-tile
     int sc[NJ][NP];
