@@ -23,7 +23,7 @@
 //                         tiles on MFMA, K split over the workgroup's waves,
 //                         SiLU(gate)*up epilogue -> h fp32
 //   requant_kernel        per (token, expert) FP8 requantisation of h
-//   chunk_down_kernel     per (expert, 128 output rows): down tiles on MFMA,
+//   chunk_down_kernel     per (expert, 256 output rows): down tiles on MFMA,
 //                         epilogue scales by s2 -> y
 //   combine_kernel        out[t] = sum over the token's K pairs of w * y, in
 //                         selection order (no float atomics)
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 // y[pos, n] = s2 * acc (the router weight is applied by the combine).
 // ---------------------------------------------------------------------------
 template <int H, int I, bool BY_PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void chunk_down_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void chunk_down_kernel(
     ChunkDownArgs a)
 {
     static_assert(H % kDnRows == 0 && I % 32 == 0, "chunk down row blocking");

@@ -255,7 +255,7 @@ __host__ __device__ constexpr bool gemv_shape_ok(int H, int I)
 constexpr int kChunkTiles = kChunkRows / 16;
 constexpr int kGuNJ = 2;                                // 16-row n-tiles per wave and matrix
 constexpr int kGuRows = 16 * kGuNJ;
-constexpr int kDnNJ = 2;
+constexpr int kDnNJ = 4;
 constexpr int kDnRows = 4 * 16 * kDnNJ;                 // 4 waves x NJ n-tiles x 16 rows
 constexpr int kRouterWaves = 8;
 
