@@ -15,12 +15,18 @@ Reported (one JSON line on stdout):
                write: the 8 selected experts' MXFP4 codes and scales, the bf16
                router, x and out) / wall time
   us_per_layer wall time per layer
+  steps        exactly --steps layer forwards are timed (whole-walk graph
+               replays, then a graph of the remaining layers); every hidden
+               set is also walked once in a timed region of its own
+               (per_set_walk_us_per_layer)
   m4           the same at 4 tokens (the speculative-decoding verify window)
-  roofline     the gate/up kernel (the largest byte stream) against 8 TB/s:
-               its algorithmic bytes (the selected experts' gate/up codes and
-               scales) over its execution time, from start/stop HIP events its
-               launch stamps (plain launches on the bench stream)
-  by_tokens    the same per token count of --tokens (1..8)
+               with natural routing; m4_32 and m4_20 with the verify-window
+               router construction (32 distinct experts, or 4 shared + 4 own
+               per token: 20)
+  roofline     the dominant kernel against 8 TB/s: its algorithmic bytes over
+               its execution time, from start/stop HIP events its launch
+               stamps on the bench stream
+  by_tokens    the same per workload
   shared_expert  the walk again with the model's shared expert in every layer
   chunk        the 512-token chunk layer (grouped scaled FP4xFP8 MFMA) and its
                matrix-core rate against the FP4 and FP8 dense peaks
@@ -59,12 +65,15 @@ def layer_bytes(n_act: int, M: int) -> int:
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20000, help="timed layer forwards (rounded up to whole walks)")
+    p.add_argument("--steps", type=int, default=20000, help="timed layer forwards (exactly this many)")
     p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--layers", type=int, default=40)
     p.add_argument("--reps", type=int, default=8, help="independent hidden sets (one graph each)")
     p.add_argument("--plain-steps", type=int, default=2000, help="layer forwards timed with plain launches")
-    p.add_argument("--cpu-layers", type=int, default=8, help="oracle layers in the CPU baseline (0: skip)")
+    p.add_argument("--cpu-runs", type=int, default=3,
+                   help="oracle runs per token count in the CPU baseline, median reported (0: skip)")
+    p.add_argument("--no-verify", dest="verify", action="store_false",
+                   help="skip the 4-token verify-window router constructions (32 and 20 distinct experts)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     p.add_argument("--tokens", type=str, default="1,4", help="token counts to time (the first is the reported value)")
@@ -115,157 +124,16 @@ def main() -> int:
     ws = moe.workspace(shp, 8)
     out = torch.empty((8, H), dtype=torch.float32, device="cuda")
 
-    def fwd(l, x, M, events=None, shared=False):
-        Ly = stack[l]
-        if shared:
-            moe.moe_decode_forward_shared(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"],
-                                          shared_layers[l], out, ws)
-        elif events is None:
-            moe.moe_decode_forward(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws)
-        else:
-            moe.moe_decode_forward_events(shp, M, x, Ly["wr"], Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws,
-                                          events)
-
+    workloads = []
+    for M in [int(v) for v in args.tokens.split(",")]:
+        workloads.append((str(M), M, None))
+        if M == 4 and args.verify:
+            # the verify window as configured: biased routers giving 32
+            # distinct experts, or 4 shared + 4 own per token (20 distinct)
+            workloads += [("4x32", 4, 32), ("4x20", 4, 20)]
     results = {}
-    kernel_stats = {}
-    shared_results = {}
-    token_counts = [int(v) for v in args.tokens.split(",")]
-    for M in token_counts:
-        xs = synth.device_hidden(L * reps, M, H, seed=10_000 + M)
-        # routing pre-pass: distinct experts of every (hidden set, layer)
-        ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
-        wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
-        n_active = torch.zeros((reps, L), dtype=torch.int32, device="cuda")
-        stream.wait_stream(torch.cuda.current_stream())   # inputs were made on the default stream
-        with torch.cuda.stream(stream):
-            for r in range(reps):
-                for l in range(L):
-                    moe.moe_route(shp, M, xs[r * L + l], stack[l]["wr"], ids, wts, ws,
-                                  taps={"n_active": n_active[r, l:l + 1]})
-        torch.cuda.synchronize()
-        n_act = n_active.cpu().numpy().astype(np.int64)
-        if n_act.min() < K or n_act.max() > min(E, M * K):
-            raise RuntimeError(f"routing pre-pass read back distinct-expert counts outside [{K}, {min(E, M * K)}]: "
-                               f"min {n_act.min()}, max {n_act.max()}")
-        rep_bytes = [sum(layer_bytes(int(n_act[r, l]), M) for l in range(L)) for r in range(reps)]
-
-        with torch.cuda.stream(stream):
-            for r in range(reps):                                  # eager warm-up walk of every set
-                for l in range(L):
-                    fwd(l, xs[r * L + l], M)
-            torch.cuda.synchronize()
-            graphs = []
-            for r in range(reps):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for l in range(L):
-                        fwd(l, xs[r * L + l], M)
-                graphs.append(g)
-        n_warm = max(1, math.ceil(args.warmup / L))
-        n_timed = max(1, math.ceil(args.steps / L))
-        with torch.cuda.stream(stream):
-            for i in range(n_warm):
-                graphs[i % reps].replay()
-            torch.cuda.synchronize()
-            t0 = torch.cuda.Event(enable_timing=True)
-            t1 = torch.cuda.Event(enable_timing=True)
-            wall0 = time.perf_counter()
-            t0.record(stream)
-            for i in range(n_timed):
-                graphs[i % reps].replay()
-            t1.record(stream)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - wall0
-        ms = t0.elapsed_time(t1)
-        steps = n_timed * L
-        total_bytes = sum(rep_bytes[i % reps] for i in range(n_timed))
-        gbs = total_bytes / (ms * 1e-3) / 1e9
-        log(f"M={M}: graph replay {steps} layers in {ms:.2f} ms ({ms * 1e3 / steps:.2f} us/layer, {gbs:.0f} GB/s, "
-            f"host wall {wall * 1e3:.1f} ms), mean distinct experts {n_act.mean():.2f}")
-
-        # plain launches (no graph)
-        n_plain = max(L, args.plain_steps)
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            p0 = torch.cuda.Event(enable_timing=True)
-            p1 = torch.cuda.Event(enable_timing=True)
-            p0.record(stream)
-            pbytes = 0
-            for i in range(n_plain):
-                r, l = (i // L) % reps, i % L
-                fwd(l, xs[r * L + l], M)
-                pbytes += layer_bytes(int(n_act[r, l]), M)
-            p1.record(stream)
-            torch.cuda.synchronize()
-        pms = p0.elapsed_time(p1)
-
-        # per-kernel durations from start/stop HIP events that each kernel's
-        # launch stamps with its own execution interval (plain launches; a
-        # spin kernel at the head of the stream lets the host queue the whole
-        # walk first, so the kernels run back to back as in the timed walk)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
-        dur = {"router": [], "gate_up": [], "down": []}
-        with torch.cuda.stream(stream):
-            for row in evs:
-                for e in row:
-                    e.record(stream)          # torch creates the HIP event on first record
-            gu_launch_bytes = []
-            for ps in range(max(2, 400 // L)):
-                r = ps % reps
-                torch.cuda._sleep(50_000_000)
-                for l in range(L):
-                    fwd(l, xs[r * L + l], M, events=evs[l])
-                torch.cuda.synchronize()
-                for l in range(L):
-                    for k, name in enumerate(("router", "gate_up", "down")):
-                        dur[name].append(evs[l][2 * k].elapsed_time(evs[l][2 * k + 1]))
-                    gu_launch_bytes.append(int(n_act[r, l]) * W13_BYTES)
-        kmean = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}   # microseconds
-        gu_bytes = float(np.mean(gu_launch_bytes))
-        kernel_stats[M] = {"us": kmean, "gate_up_bytes": gu_bytes,
-                           "gate_up_gbs": gu_bytes / (kmean["gate_up"] * 1e-6) / 1e9}
-        log(f"M={M}: kernel means (us) {kmean}, gate_up {kernel_stats[M]['gate_up_gbs']:.0f} GB/s")
-
-        if shared_layers is not None:
-            # the same walk with the model's shared expert in every layer
-            # (one more expert's weights per layer, same kernels)
-            with torch.cuda.stream(stream):
-                for r in range(reps):
-                    for l in range(L):
-                        fwd(l, xs[r * L + l], M, shared=True)
-                torch.cuda.synchronize()
-                gsh = []
-                for r in range(reps):
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=stream):
-                        for l in range(L):
-                            fwd(l, xs[r * L + l], M, shared=True)
-                    gsh.append(g)
-                for i in range(reps):
-                    gsh[i].replay()
-                torch.cuda.synchronize()
-                n_sh = max(1, math.ceil(args.shared_steps / L))
-                s0 = torch.cuda.Event(enable_timing=True)
-                s1 = torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
-                for i in range(n_sh):
-                    gsh[i % reps].replay()
-                s1.record(stream)
-                torch.cuda.synchronize()
-            sms = s0.elapsed_time(s1)
-            sbytes = sum(rep_bytes[i % reps] + L * EXPERT_BYTES for i in range(n_sh))
-            shared_results[M] = {"us_per_layer": round(sms * 1e3 / (n_sh * L), 3),
-                                 "gbs": round(sbytes / (sms * 1e-3) / 1e9, 1),
-                                 "pct_of_hbm_peak": round(100 * sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                                 "layers": n_sh * L}
-            log(f"M={M} with a shared expert: {shared_results[M]['us_per_layer']:.2f} us/layer, "
-                f"{shared_results[M]['gbs']:.0f} GB/s")
-            del gsh
-
-        results[M] = {"us_per_layer": ms * 1e3 / steps, "gbs": gbs, "steps": steps, "ms": ms,
-                      "mean_distinct_experts": float(n_act.mean()),
-                      "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9}
-        del graphs, xs
+    for name, M, distinct in workloads:
+        results[name] = time_walks(args, moe, synth, stack, shared_layers, shp, stream, ws, out, name, M, distinct)
 
     lm_head = None
     if args.lm_head_vocab > 0:
@@ -276,60 +144,237 @@ def main() -> int:
         chunk = chunk_bench(args, moe, synth, stack, shp, stream)
 
     cpu = None
-    if args.cpu_layers > 0:
-        cpu = cpu_baseline(args.cpu_layers)
+    if args.cpu_runs > 0:
+        cpu = cpu_baseline(args.cpu_runs)
 
-    r1 = results[token_counts[0]]
-    k1 = kernel_stats[token_counts[0]]
-    m4 = None
-    if 4 in results:
-        r4 = results[4]
-        m4 = {"us_per_layer": round(r4["us_per_layer"], 3), "gbs": round(r4["gbs"], 1),
-              "pct_of_hbm_peak": round(100 * r4["gbs"] / HBM_PEAK_GBS, 2),
-              "mean_distinct_experts": round(r4["mean_distinct_experts"], 2),
-              "plain_us_per_layer": round(r4["plain_us_per_layer"], 3),
-              "kernel_us": {k: round(v, 3) for k, v in kernel_stats[4]["us"].items()},
-              "gate_up_gbs": round(kernel_stats[4]["gate_up_gbs"], 1)}
-    by_tokens = {str(M): {"us_per_layer": round(results[M]["us_per_layer"], 3), "gbs": round(results[M]["gbs"], 1),
-                          "pct_of_hbm_peak": round(100 * results[M]["gbs"] / HBM_PEAK_GBS, 2),
-                          "mean_distinct_experts": round(results[M]["mean_distinct_experts"], 2),
-                          "plain_us_per_layer": round(results[M]["plain_us_per_layer"], 3),
-                          "kernel_us": {k: round(v, 3) for k, v in kernel_stats[M]["us"].items()}}
-                 for M in token_counts}
+    head = results[workloads[0][0]]
+
+    def summary(r):
+        return {"us_per_layer": round(r["us_per_layer"], 3), "gbs": round(r["gbs"], 1),
+                "pct_of_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
+                "distinct_experts": round(r["mean_distinct_experts"], 2),
+                "per_set_walk_us_per_layer": r["per_set"],
+                "plain_us_per_layer": round(r["plain_us_per_layer"], 3),
+                "kernel_us": {k: round(v, 3) for k, v in r["kernel_us"].items()}}
+
     traffic = measured_traffic()
+    rl = head["roofline"]
     line = {
         "metric": "MoE-layer decode us + weight-stream HBM GB/s (% of peak), M=1 and M=4",
-        "value": round(r1["gbs"], 1),
+        "value": round(head["gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": r1["steps"],
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": r1["ms"] / r1["steps"],
+        "ms_per_step": head["ms"] / head["steps"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp4 x e4m3 -> f32",
         "data": "synthetic",
-        "config": {"workload": f"ling-shaped MoE decode layer, {token_counts[0]} token(s), cold walk over {L} layers",
-                   "hidden": H, "expert_inter": I, "experts": E, "topk": K, "tokens": token_counts[0], "layers": L,
-                   "launch": f"hip graph per {L}-layer walk"},
-        "us_per_layer": round(r1["us_per_layer"], 3),
-        "pct_of_hbm_peak": round(100 * r1["gbs"] / HBM_PEAK_GBS, 2),
-        "plain_launch": {"us_per_layer": round(r1["plain_us_per_layer"], 3), "gbs": round(r1["plain_gbs"], 1)},
-        "m4": m4,
-        "by_tokens": by_tokens,
-        "kernel_us": {k: round(v, 3) for k, v in k1["us"].items()},
-        "roofline": {"kernel": "gate_up_kernel<H=2560,I=768> (1 token)", "bound": "hbm",
-                     "achieved": round(k1["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k1["gate_up_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": k1["gate_up_bytes"], "us_per_launch": round(k1["us"]["gate_up"], 3)},
-        "shared_expert": {"by_tokens": {str(M): v for M, v in shared_results.items()}} if shared_results else None,
+        "config": {"workload": f"ling-shaped MoE decode layer, {workloads[0][1]} token(s), cold walk over {L} layers",
+                   "hidden": H, "expert_inter": I, "experts": E, "topk": K, "tokens": workloads[0][1], "layers": L,
+                   "launch": f"hip graphs of the {L}-layer walk; the timed region is exactly --steps layers"},
+        "us_per_layer": round(head["us_per_layer"], 3),
+        "pct_of_hbm_peak": round(100 * head["gbs"] / HBM_PEAK_GBS, 2),
+        "per_set_walk_us_per_layer": head["per_set"],
+        "plain_launch": {"us_per_layer": round(head["plain_us_per_layer"], 3), "gbs": round(head["plain_gbs"], 1)},
+        "m4": summary(results["4"]) if "4" in results else None,
+        "m4_32": summary(results["4x32"]) if "4x32" in results else None,
+        "m4_20": summary(results["4x20"]) if "4x20" in results else None,
+        "by_tokens": {n: summary(r) for n, r in results.items()},
+        "kernel_us": {k: round(v, 3) for k, v in head["kernel_us"].items()},
+        "roofline": {"kernel": rl["kernel"], "bound": "hbm", "achieved": round(rl["gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(rl["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": rl["bytes"], "us_per_launch": round(rl["us"], 3),
+                     "timing": rl["timing"]},
+        "shared_expert": {"by_tokens": {n: r["shared"] for n, r in results.items() if r.get("shared")}} or None,
         "chunk": chunk,
         "lm_head": lm_head,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_walks(args, moe, synth, stack, shared_layers, shp, stream, ws, out, name, M, distinct) -> dict:
+    """One decode workload (M tokens; natural routing, or the verify-window
+    router construction with `distinct` experts) over the cold walk: a HIP
+    graph per hidden set of the whole walk; exactly args.steps layers timed
+    (whole walks, then a prefix graph for the rest); every hidden set timed as
+    one walk of its own; plain launches; per-kernel launch-stamped events."""
+    import numpy as np
+    import torch
+    L, reps = len(stack), args.reps
+    xs = synth.device_hidden(L * reps, M, H, seed=10_000 + M + (0 if distinct is None else 1000 * distinct))
+    if distinct is None:
+        routers = [[stack[l]["wr"] for l in range(L)] for _ in range(reps)]
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(20_000 + distinct)
+        routers = [[synth.device_verify_router(stack[l]["wr"], xs[r * L + l], distinct, g, K=K) for l in range(L)]
+                   for r in range(reps)]
+    torch.cuda.synchronize()
+
+    def fwd(r, l, events=None, shared=False):
+        Ly, x, wr = stack[l], xs[r * L + l], routers[r][l]
+        if shared:
+            moe.moe_decode_forward_shared(shp, M, x, wr, Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"],
+                                          shared_layers[l], out, ws)
+        elif events is None:
+            moe.moe_decode_forward(shp, M, x, wr, Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws)
+        else:
+            moe.moe_decode_forward_events(shp, M, x, wr, Ly["w13"], Ly["s13"], Ly["w2"], Ly["s2"], out, ws, events)
+
+    # routing pre-pass: distinct experts of every (hidden set, layer)
+    ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    n_active = torch.zeros((reps, L), dtype=torch.int32, device="cuda")
+    stream.wait_stream(torch.cuda.current_stream())      # inputs were made on the default stream
+    with torch.cuda.stream(stream):
+        for r in range(reps):
+            for l in range(L):
+                moe.moe_route(shp, M, xs[r * L + l], routers[r][l], ids, wts, ws,
+                              taps={"n_active": n_active[r, l:l + 1]})
+    torch.cuda.synchronize()
+    n_act = n_active.cpu().numpy().astype(np.int64)
+    lo, hi = (K, min(E, M * K)) if distinct is None else (distinct, distinct)
+    if n_act.min() < lo or n_act.max() > hi:
+        raise RuntimeError(f"{name}: routing pre-pass read back distinct-expert counts outside [{lo}, {hi}]: "
+                           f"min {n_act.min()}, max {n_act.max()}")
+    lb = [[layer_bytes(int(n_act[r, l]), M) for l in range(L)] for r in range(reps)]
+
+    with torch.cuda.stream(stream):
+        for r in range(reps):                               # eager warm-up walk of every set
+            for l in range(L):
+                fwd(r, l)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for l in range(L):
+                    fwd(r, l)
+            graphs.append(g)
+        n_full, rest = divmod(args.steps, L)
+        prefix = None
+        if rest:
+            prefix = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(prefix, stream=stream):
+                for l in range(rest):
+                    fwd(n_full % reps, l)
+        # untimed warm-up: --warmup layers, as whole walks
+        for i in range(max(1, math.ceil(args.warmup / L))):
+            graphs[i % reps].replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(n_full):
+            graphs[i % reps].replay()
+        if prefix is not None:
+            prefix.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        steps = n_full * L + rest
+        total = sum(sum(lb[i % reps]) for i in range(n_full)) + sum(lb[n_full % reps][:rest])
+        # every hidden set walked once, each in a timed region of its own
+        per_set = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graphs[r].replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per_set.append(a.elapsed_time(b) * 1e3 / L)
+    gbs = total / (ms * 1e-3) / 1e9
+    log(f"{name}: graph replay of exactly {steps} layers in {ms:.3f} ms ({ms * 1e3 / steps:.2f} us/layer, "
+        f"{gbs:.0f} GB/s); every set walked once: median {np.median(per_set):.2f} us/layer "
+        f"(min {min(per_set):.2f}, max {max(per_set):.2f}); mean distinct experts {n_act.mean():.2f}")
+
+    # plain launches (no graph)
+    n_plain = max(L, args.plain_steps)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        pbytes = 0
+        for i in range(n_plain):
+            r, l = (i // L) % reps, i % L
+            fwd(r, l)
+            pbytes += lb[r][l]
+        p1.record(stream)
+        torch.cuda.synchronize()
+    pms = p0.elapsed_time(p1)
+
+    # per-kernel durations from start/stop HIP events stamped by each kernel's
+    # own launch (plain launches on the bench stream; a spin kernel at the
+    # head of the stream lets the host queue the whole walk first, so the
+    # kernels run back to back as in the timed walk)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+    names = ("router", "gate_up", "down")
+    dur = {k: [] for k in names}
+    gu_launch_bytes = []
+    with torch.cuda.stream(stream):
+        for row in evs:
+            for e in row:
+                e.record(stream)          # torch creates the HIP event on first record
+        for ps in range(max(2, 400 // L)):
+            r = ps % reps
+            torch.cuda._sleep(50_000_000)
+            for l in range(L):
+                fwd(r, l, events=evs[l])
+            torch.cuda.synchronize()
+            for l in range(L):
+                for k, kn in enumerate(names):
+                    dur[kn].append(evs[l][2 * k].elapsed_time(evs[l][2 * k + 1]))
+                gu_launch_bytes.append(int(n_act[r, l]) * W13_BYTES)
+    kus = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}
+    gu_bytes = float(np.mean(gu_launch_bytes))
+    log(f"{name}: kernel means (us) {kus}")
+
+    shared = None
+    if shared_layers is not None and distinct is None:
+        # the same walk with the model's shared expert in every layer
+        with torch.cuda.stream(stream):
+            for r in range(reps):
+                for l in range(L):
+                    fwd(r, l, shared=True)
+            torch.cuda.synchronize()
+            gsh = []
+            for r in range(reps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for l in range(L):
+                        fwd(r, l, shared=True)
+                gsh.append(g)
+            for i in range(reps):
+                gsh[i].replay()
+            torch.cuda.synchronize()
+            n_sh = max(reps, math.ceil(args.shared_steps / L))
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for i in range(n_sh):
+                gsh[i % reps].replay()
+            s1.record(stream)
+            torch.cuda.synchronize()
+        sms = s0.elapsed_time(s1)
+        sbytes = sum(sum(lb[i % reps]) + L * EXPERT_BYTES for i in range(n_sh))
+        shared = {"us_per_layer": round(sms * 1e3 / (n_sh * L), 3), "gbs": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                  "pct_of_hbm_peak": round(100 * sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), "layers": n_sh * L}
+        log(f"{name} with a shared expert: {shared['us_per_layer']:.2f} us/layer, {shared['gbs']:.0f} GB/s")
+        del gsh
+    del graphs, prefix
+    return {"us_per_layer": ms * 1e3 / steps, "gbs": gbs, "steps": steps, "ms": ms,
+            "per_set": {"median": round(float(np.median(per_set)), 3), "min": round(min(per_set), 3),
+                        "max": round(max(per_set), 3), "sets": reps},
+            "mean_distinct_experts": float(n_act.mean()),
+            "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9,
+            "kernel_us": kus, "shared": shared,
+            "roofline": {"kernel": f"gate_up_kernel<H=2560,I=768> ({M} token(s))", "bytes": gu_bytes,
+                         "us": kus["gate_up"], "gbs": gu_bytes / (kus["gate_up"] * 1e-6) / 1e9,
+                         "timing": "launch-stamped HIP events, plain launches queued behind a spin kernel"}}
 
 
 def lm_head_bench(args, moe, stream) -> dict:
@@ -517,28 +562,50 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(n_layers: int) -> dict:
-    """The oracle, single-threaded, on n_layers Ling-shaped 1-token layers."""
+def cpu_baseline(runs: int) -> dict:
+    """The oracle on the bench's own workload: one Ling-shaped layer at 1 token
+    (natural routing) and at 4 tokens (the verify construction with 32 distinct
+    experts), each timed `runs` times inside the oracle library around the
+    layer call only, with the process pinned to one host core; the median is
+    reported.  The oracle is single-threaded."""
+    import platform
+
     import numpy as np
 
     import oracle
     from mxfp4_weight_streaming_amd import synth
-    log(f"cpu baseline: oracle on {n_layers} layers")
+    log("cpu baseline: drawing the oracle's inputs")
     w = synth.expert_weights(77, H, I, E)
+    x1 = synth.decode_tokens(500, w, 1, K).x
+    v4 = synth.verify_router(501, w, 32, M=4, K=K)
     oracle.lib()
-    total = 0
-    t0 = time.perf_counter()
-    for i in range(n_layers):
-        rng = np.random.default_rng(500 + i)
-        wr = synth.normal_bf16(rng, (E, H), 0.02)
-        x = synth.normal_bf16(rng, (1, H), 1.0)
-        oracle.moe_layer(x, wr, w.w13, w.s13, w.w2, w.s2, K)
-        total += layer_bytes(K, 1)
-    dt = time.perf_counter() - t0
-    log(f"cpu baseline: {dt:.1f} s")
-    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_layers} Ling-shaped 1-token layers (H=2560, I=768, E=256, K=8), "
-                      f"{dt / n_layers * 1e3:.0f} ms per layer on one host core"}
+    model = platform.processor() or "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        s1 = oracle.time_layer(x1, w.wr, w.w13, w.s13, w.w2, w.s2, K, runs=runs)
+        s4 = oracle.time_layer(v4.x, v4.wts.wr, w.w13, w.s13, w.w2, w.s2, K, runs=runs)
+    finally:
+        os.sched_setaffinity(0, allowed)
+    m1, m4 = float(np.median(s1)), float(np.median(s4))
+    log(f"cpu baseline: 1 token {m1:.3f} s, 4 tokens {m4:.3f} s per layer on core {core} ({model})")
+    b1, b4 = layer_bytes(K, 1), layer_bytes(32, 4)
+    return {"value": round(b1 / m1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one Ling-shaped layer (H=2560, I=768, E=256, K=8) at 1 token: median of {runs} runs "
+                      f"{m1 * 1e3:.0f} ms ({[round(v * 1e3) for v in s1]} ms); at 4 tokens with 32 distinct "
+                      f"experts: {m4 * 1e3:.0f} ms ({b4 / m4 / 1e9:.4f} GB/s); timed inside the oracle library "
+                      f"(CLOCK_MONOTONIC around the layer call), process pinned to core {core}",
+            "us_per_layer": {"1": round(m1 * 1e6, 1), "4x32": round(m4 * 1e6, 1)},
+            "host": {"cpu_model": model, "nproc": os.cpu_count(), "cores_allowed": len(allowed),
+                     "pinned_core": core}}
 
 
 if __name__ == "__main__":

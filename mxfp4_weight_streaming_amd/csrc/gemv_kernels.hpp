@@ -133,6 +133,55 @@ __device__ void compact_wave(int P, int K, RouteLds& r)
     else compact_wave_t<64>(P, K, r);
 }
 
+// Compaction of the ids in r.ids (and the shared expert's slot), by wave 0;
+// the caller synchronises before and after.  distinct: the ids of the one
+// token are known to be distinct (routed by top-K), which takes a fast path.
+__device__ void route_compact(int M, int K, bool distinct, int shared, RouteLds& r)
+{
+    const int tid = threadIdx.x, P = M * K;
+    if ((tid >> 6) != 0) return;
+    if (M == 1 && distinct) {
+        // one token routed here: its K experts are distinct, so the slots
+        // are the experts in ascending id and slot s holds exactly one
+        // pair (caller ids may repeat an expert: they take the general
+        // compaction)
+        const int lane = tid & 63;
+        const int4 a4 = *reinterpret_cast<const int4*>(r.ids), b4 = *reinterpret_cast<const int4*>(r.ids + 4);
+        const int all[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        const int e = r.ids[lane & (kMaxTopK - 1)];
+        int slot = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) slot += (k < K) && all[k] < e;
+        if (lane < K) {
+            r.act_experts[slot] = e;
+            r.offsets[slot] = slot;
+            r.pair_token[slot] = 0;
+            r.pair_src[slot] = lane;
+        }
+        if (lane == 0) {
+            r.n_act = K;
+            r.offsets[K] = K;
+        }
+    } else {
+        compact_wave(P, K, r);
+    }
+    if (shared) {
+        // the shared expert's slot follows the routed ones: every token,
+        // pair row P + t (its weight, 1, is applied by the down kernel)
+        const int lane = tid & 63;
+        if (lane < M) {
+            r.pair_token[P + lane] = lane;
+            r.pair_src[P + lane] = P + lane;
+        }
+        if (lane == 0) {
+            const int n = r.n_act;
+            r.act_experts[n] = kSharedExpert;
+            r.offsets[n + 1] = P + M;
+            r.n_act = n + 1;
+        }
+    }
+}
+
 __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
 {
     const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
@@ -144,48 +193,7 @@ __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
         for (int i = tid; i < P; i += blockDim.x) r.ids[i] = min(max(src.ids[i], 0), E - 1);   // clamped, never OOB
     }
     __syncthreads();
-    if (wave == 0) {
-        if (M == 1 && src.logits != nullptr) {
-            // one token routed here: its K experts are distinct, so the slots
-            // are the experts in ascending id and slot s holds exactly one
-            // pair (caller ids may repeat an expert: they take the general
-            // compaction)
-            const int lane = tid & 63;
-            const int4 a4 = *reinterpret_cast<const int4*>(r.ids), b4 = *reinterpret_cast<const int4*>(r.ids + 4);
-            const int all[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-            const int e = r.ids[lane & (kMaxTopK - 1)];
-            int slot = 0;
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) slot += (k < K) && all[k] < e;
-            if (lane < K) {
-                r.act_experts[slot] = e;
-                r.offsets[slot] = slot;
-                r.pair_token[slot] = 0;
-                r.pair_src[slot] = lane;
-            }
-            if (lane == 0) {
-                r.n_act = K;
-                r.offsets[K] = K;
-            }
-        } else {
-            compact_wave(P, K, r);
-        }
-        if (src.shared) {
-            // the shared expert's slot follows the routed ones: every token,
-            // pair row P + t (its weight, 1, is applied by the down kernel)
-            const int lane = tid & 63;
-            if (lane < M) {
-                r.pair_token[P + lane] = lane;
-                r.pair_src[P + lane] = P + lane;
-            }
-            if (lane == 0) {
-                const int n = r.n_act;
-                r.act_experts[n] = kSharedExpert;
-                r.offsets[n + 1] = P + M;
-                r.n_act = n + 1;
-            }
-        }
-    }
+    route_compact(M, K, src.logits != nullptr, src.shared, r);
     __syncthreads();
 }
 
@@ -210,8 +218,9 @@ __device__ void publish_route(const RouteLds& r, const RouteSrc& src, int32_t* i
 // One token routed from its logits, in the gate/up kernel.  The workgroup's
 // slots are ranks: slot s < K is the rank-s expert with pair s (token 0), and
 // slot K the shared expert with pair K.  The weights of a slot are needed
-// before the rest of the routing, so wave 0 ranks only up to the workgroup's
-// own slot (slot_me) and the loads go out as soon as that expert is known;
+// before the rest of the routing, so wave 0 ranks only up to slot_me, the
+// highest slot among the workgroup's items, and the loads go out as soon as
+// those experts are known;
 // workgroup 0 ranks all K and publishes the routing and the ascending-id
 // compaction that route_prologue and publish_route would give.
 __device__ void route_rank1(const RouteSrc& src, int slot_me, RouteLds& r, int32_t* ids_out, float* w_out,
@@ -452,7 +461,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     //    kernel (and the caller).  One token routed from its logits: slots are
     //    ranks, and a workgroup ranks only up to its own slot (route_rank1).
     if (MT == 1 && a.src.logits != nullptr) {
-        route_rank1(a.src, min((int)blockIdx.x / BPE, a.src.K), rl, a.ids_out, a.w_out, a.cp);
+        // the workgroup's items are blockIdx.x, + gridDim.x, ...: it ranks up
+        // to the slot of its last one (the item count, (K + shared) * BPE, is
+        // known before the routing: one token's K experts are distinct)
+        const int n1 = (a.src.K + a.src.shared) * BPE;
+        int last = blockIdx.x;
+        if (last < n1) last += ((n1 - 1 - last) / (int)gridDim.x) * (int)gridDim.x;
+        route_rank1(a.src, min(last / BPE, a.src.K), rl, a.ids_out, a.w_out, a.cp);
     } else {
         route_prologue(a.src, rl);
         if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);

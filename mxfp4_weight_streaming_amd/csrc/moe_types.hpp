@@ -175,6 +175,50 @@ struct CombineArgs {
     int shared;            // 1: add the shared expert's row y[pos_of[M*K + t]] (weight 1)
 };
 
+// The one-kernel decode layer (M <= kMaxGemvTokens).  Its workgroups hand
+// results to each other through epoch-tagged 64-bit words in the workspace:
+// the high half holds the tag of the call that wrote the word (the epoch read
+// at the call's start, plus one), the low half the fp32 value.  Each word is
+// written and read whole by relaxed device-scope atomics, so a reader that
+// sees its own call's tag has the value, with no fences.  The region is
+// zeroed once by moe_workspace_init; its layout does not depend on M.
+struct LayerSync {
+    uint32_t* word;        // [0] epoch of the last call, [1] sticky error bits
+    uint64_t* arrive;      // [kMaxLayerBlocks] one word per workgroup
+    uint64_t* logits;      // [kMaxGemvTokens, E]
+    uint64_t* h;           // [kMaxPairsExt, I] gate/up output, pair order
+    uint64_t* y;           // [kMaxPairsExt, H] weighted down output, pair order
+};
+constexpr int kMaxLayerBlocks = 1024;
+// error bits of LayerSync::word[1] (a bounded wait ran out)
+enum : uint32_t { kWaitLogits = 1u, kWaitH = 2u, kWaitY = 4u, kWaitArrive = 8u };
+
+struct LayerArgs {
+    // routed from x and wr (x != nullptr), or from the caller's ids, weights
+    // and FP8 activations
+    const uint16_t* x;     // [M,H] bf16
+    const uint16_t* wr;    // [E,H] bf16
+    const uint8_t* act_q;  // [M,H] E4M3 (x == nullptr)
+    const float* act_s;    // [M]
+    const int32_t* ids;    // [M,K] (x == nullptr), clamped into [0, E)
+    const float* topk_w;   // [M,K]
+    int M, E, K, shared;
+    const uint8_t* w13;    // [E,2I,H/2]
+    const uint8_t* s13;    // [E,2I,H/32]
+    const uint8_t* w2;     // [E,H,I/2]
+    const uint8_t* sw2;    // [E,H,I/32]
+    SharedWeights sh;
+    float* out;            // [M,H]
+    // optional taps in pair order (rows M*K + t: the shared expert)
+    float* h_tap;          // [M*K (+M),I]
+    uint8_t* q2_tap;       // [M*K (+M),I]
+    float* s2_tap;         // [M*K (+M)]
+    int32_t* ids_out;      // [M,K] routed ids (x != nullptr)
+    float* w_out;          // [M,K] their weights
+    LayerSync sync;
+    uint64_t wait_ticks;   // bound of every wait, in s_memrealtime ticks
+};
+
 // ---------------------------------------------------------------------------
 // Shape geometry, as constexpr functions so that the kernel templates and the
 // host launchers (which also launch kernels compiled at run time for shapes
@@ -250,8 +294,40 @@ __host__ __device__ constexpr bool gemv_shape_ok(int H, int I)
            I % gate_up_rows_per_block(H) == 0 && H % down_rows_per_block(H, I) == 0;
 }
 
+// One-kernel decode layer blocking.  A gate/up task is one wave's share of
+// one slot: 64 / LPR row pairs (gate row r and up row I + r), LPR lanes per
+// row, each lane CPL blocks of 32 (the gate/up GEMV geometry above).  A down
+// task is one wave's share of one slot: DP passes of 64 / LD output rows, LD
+// lanes per row, each lane CD blocks of 32 per pass; LD is the largest power
+// of two up to 16 dividing I / 32.  Tasks are dealt out to the workgroups in
+// equal contiguous ranges (slot-major), and to a workgroup's 8 waves in turn.
+__host__ __device__ constexpr int layer_down_lanes(int I)
+{
+    return ((I / 32) % 16 == 0) ? 16 : ((I / 32) % 8 == 0) ? 8 : ((I / 32) % 4 == 0) ? 4 : ((I / 32) % 2 == 0) ? 2 : 1;
+}
+__host__ __device__ constexpr int layer_down_blocks(int I) { return (I / 32) / layer_down_lanes(I); }
+__host__ __device__ constexpr int layer_down_rows_per_pass(int I) { return kWaveSize / layer_down_lanes(I); }
+__host__ __device__ constexpr int layer_down_passes(int H, int I)
+{
+    return (layer_down_blocks(I) <= 3 && H % (2 * layer_down_rows_per_pass(I)) == 0) ? 2 : 1;
+}
+__host__ __device__ constexpr int layer_gate_up_tasks(int H, int I) { return I / (kWaveSize / gate_up_lanes_per_row(H)); }
+__host__ __device__ constexpr int layer_down_tasks(int H, int I)
+{
+    return H / (layer_down_rows_per_pass(I) * layer_down_passes(H, I));
+}
+constexpr int kLayerWaves = 8;
+// The one-kernel layer exists for (H, I) when its register plan holds: at most
+// 5 gate/up blocks and 6 down blocks per lane and task.
+__host__ __device__ constexpr bool layer_shape_ok(int H, int I)
+{
+    return gemv_shape_ok(H, I) && (H / 32) / gate_up_lanes_per_row(H) <= 5 &&
+           layer_down_blocks(I) * layer_down_passes(H, I) <= 6 && H % (layer_down_rows_per_pass(I) * layer_down_passes(H, I)) == 0;
+}
+
 // Chunk path blocking: 16-row MFMA tiles, 64-row chunks, 32 gate/up rows and
-// 128 down rows per workgroup, router K slices of H/8.
+// 256 down rows per workgroup (4 waves x kDnNJ = 4 n-tiles of 16 rows), router
+// K slices of H/8.  The chunk path therefore needs H % 256 == 0.
 constexpr int kChunkTiles = kChunkRows / 16;
 constexpr int kGuNJ = 2;                                // 16-row n-tiles per wave and matrix
 constexpr int kGuRows = 16 * kGuNJ;

@@ -48,29 +48,15 @@ __device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b
     s[b] = sw ? sa : sb;
 }
 
-// One out-of-line body per logits-per-lane count, called through the inlined
-// dispatch below, where E is wave-uniform: every body inlined at every call
-// site made the gate/up kernels larger and slower.
+// The selection on keys already held by the lanes: lane l holds the keys of
+// experts l + 64 i in u[i] (0 for experts past E), s[i] = i.  Sorts each
+// lane's entries, then runs the R rounds; writes ids_out[0..R) and, when
+// R == K, the softmax weights w_out[0..K).
 template <int PER>
-__device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t* ids_out, float* w_out, int R)
+__device__ __forceinline__ void topk_select_t(uint32_t (&u)[PER], int (&s)[PER], int K, int32_t* ids_out,
+                                              float* w_out, int R)
 {
     const int lane = threadIdx.x & 63;
-    // the logits are in global memory: loads through a global pointer are
-    // counted by one counter and waited for together (a generic pointer gives
-    // flat loads, counted by two)
-    const __attribute__((address_space(1))) float* L = (const __attribute__((address_space(1))) float*)Lg;
-    uint32_t u[PER];
-    int s[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {             // unconditional loads: all in flight together
-        const int e = lane + kWave * i;
-        const float v = L[e < E ? e : E - 1];
-        // + 0.0f folds -0 into +0; 0 is below every key.  The mask is
-        // arithmetic, so the load's result is always used and the compiler
-        // cannot move the load into a branch (with a wait of its own)
-        u[i] = f32_orderable(v + 0.0f) & (0u - (uint32_t)(e < E));
-        s[i] = i;
-    }
     // sorting network over the lane's entries (a strict order: slots differ)
     if constexpr (PER == 2) {
         lane_sort_step<PER>(u, s, 0, 1);
@@ -124,6 +110,38 @@ __device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t*
         ids_out[lane] = my_e;
         w_out[lane] = ex / den;
     }
+}
+
+// The key of a logit: + 0.0f folds -0 into +0; 0 is below every key and
+// marks experts past E.
+__device__ __forceinline__ uint32_t topk_key(float v, bool valid)
+{
+    return f32_orderable(v + 0.0f) & (0u - (uint32_t)valid);
+}
+
+// One out-of-line body per logits-per-lane count, called through the inlined
+// dispatch below, where E is wave-uniform: every body inlined at every call
+// site made the gate/up kernels larger and slower.
+template <int PER>
+__device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t* ids_out, float* w_out, int R)
+{
+    const int lane = threadIdx.x & 63;
+    // the logits are in global memory: loads through a global pointer are
+    // counted by one counter and waited for together (a generic pointer gives
+    // flat loads, counted by two)
+    const __attribute__((address_space(1))) float* L = (const __attribute__((address_space(1))) float*)Lg;
+    uint32_t u[PER];
+    int s[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {             // unconditional loads: all in flight together
+        const int e = lane + kWave * i;
+        const float v = L[e < E ? e : E - 1];
+        // the mask is arithmetic, so the load's result is always used and
+        // the compiler cannot move the load into a branch (with a wait of its own)
+        u[i] = topk_key(v, e < E);
+        s[i] = i;
+    }
+    topk_select_t<PER>(u, s, K, ids_out, w_out, R);
 }
 
 // Top-K of one token's E logits by one wave: ids_out[r] is the rank-r expert

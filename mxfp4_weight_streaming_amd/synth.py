@@ -209,3 +209,30 @@ def device_hidden(n: int, M: int, H: int, seed: int, device="cuda"):
     g.manual_seed(seed)
     return [torch.randn((M, H), generator=g, device=device).to(torch.bfloat16).view(torch.uint16)
             for _ in range(n)]
+
+
+def device_verify_router(wr_bits, x_bits, distinct: int, gen, K: int = 8, bias: float = 0.2):
+    """The verify-window router construction of verify_router, on the device:
+    a copy of the bf16 router wr_bits [E,H] with Wr[e] += bias * u_t for the
+    experts each token t of x_bits [M,H] is meant to pick (u_t = x_t/|x_t|,
+    in float64), the experts taken from a seeded permutation (generator gen).
+    distinct == M*K: every token gets K experts of its own; otherwise 4
+    experts are shared by all tokens (bias * sum_t u_t) and every token gets
+    K - 4 of its own.  Rounded back to bf16 through binary32 as verify_router."""
+    import torch
+    M = x_bits.shape[0]
+    E = wr_bits.shape[0]
+    assert distinct in (M * K, 4 + M * (K - 4))
+    wr = wr_bits.view(torch.bfloat16).double()
+    x = x_bits.view(torch.bfloat16).double()
+    u = x / x.norm(dim=1, keepdim=True)
+    perm = torch.randperm(E, generator=gen, device=wr.device)
+    if distinct == M * K:
+        for t in range(M):
+            wr[perm[K * t:K * (t + 1)]] += bias * u[t]
+    else:
+        wr[perm[:4]] += bias * u.sum(dim=0)
+        own = K - 4
+        for t in range(M):
+            wr[perm[4 + own * t:4 + own * (t + 1)]] += bias * u[t]
+    return wr.float().to(torch.bfloat16).view(torch.uint16).contiguous()

@@ -74,6 +74,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_requant.argtypes = [_I, _I, _P, _P, _P]
     L.orc_down_combine.restype = None
     L.orc_down_combine.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    L.orc_time_layer.restype = None
+    L.orc_time_layer.argtypes = [_I, _I, _I, _I, _I, _I] + [_P] * 17
     L.orc_lm_head_quant.restype = None
     L.orc_lm_head_quant.argtypes = [_I, _I, _P, _P, _P]
     L.orc_lm_head_gemv.restype = None
@@ -261,6 +263,25 @@ def moe_layer(x, wr, w13, s13, w2, sc2, K: int, shared: SharedExpert | None = No
         out = out + down_combine(q2s, s2s, zero, np.ones((M, 1)), shared.w2[None], shared.s2[None], H)
         h, q2, s2 = np.vstack([h, hs]), np.vstack([q2, q2s]), np.concatenate([s2, s2s])
     return LayerTaps(r, q, s, h, q2, s2, out)
+
+
+def time_layer(x, wr, w13, s13, w2, sc2, K: int, runs: int = 3) -> np.ndarray:
+    """Wall time (seconds) of each of `runs` calls of the oracle's whole layer on
+    the same inputs, clocked inside the oracle library around the call only
+    (the CPU baseline; every buffer is made before the first run)."""
+    x = _c(x, np.uint16)
+    wr = _c(wr, np.uint16)
+    w13, s13, w2, sc2 = (_c(a, np.uint8) for a in (w13, s13, w2, sc2))
+    M, H = x.shape
+    E = wr.shape[0]
+    I = w2.shape[2] * 2
+    bufs = [np.zeros((M, E)), np.zeros((M, K), np.int32), np.zeros((M, K)), np.zeros(M),
+            np.zeros((M, H), np.uint8), np.zeros(M, np.float32), np.zeros((M * K, I)),
+            np.zeros((M * K, I), np.uint8), np.zeros(M * K, np.float32), np.zeros((M, H))]
+    sec = np.zeros(runs)
+    lib().orc_time_layer(runs, M, H, I, E, K, _ptr(x), _ptr(wr), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(sc2),
+                         *[_ptr(b) for b in bufs], _ptr(sec))
+    return sec
 
 
 def lm_head_quant(w: np.ndarray):

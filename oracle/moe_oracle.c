@@ -26,9 +26,11 @@
  *
  * Parity pins for every function live in tests/test_oracle_pins.py.
  */
+#define _POSIX_C_SOURCE 199309L
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <time.h>
 
 /* ------------------------------------------------------------------------- */
 /* Number formats                                                             */
@@ -328,6 +330,27 @@ void orc_moe_layer(int M, int H, int I, int E, int K,
     orc_gate_up(M, H, I, K, q, s, ids, w13, s13, h);
     orc_requant(M * K, I, h, q2, s2);
     orc_down_combine(M, H, I, K, q2, s2, ids, w, w2, sc2, out);
+}
+
+/* The CPU baseline: runs orc_moe_layer `runs` times on the same inputs and
+ * writes each run's wall time in seconds (CLOCK_MONOTONIC around the call
+ * only; the inputs and outputs are the caller's, made before the first run).
+ * No arithmetic of its own. */
+void orc_time_layer(int runs, int M, int H, int I, int E, int K,
+                    const uint16_t* x, const uint16_t* wr,
+                    const uint8_t* w13, const uint8_t* s13,
+                    const uint8_t* w2, const uint8_t* sc2,
+                    double* logits, int32_t* ids, double* w, double* gap,
+                    uint8_t* q, float* s, double* h, uint8_t* q2, float* s2,
+                    double* out, double* seconds)
+{
+    for (int r = 0; r < runs; ++r) {
+        struct timespec a, b;
+        clock_gettime(CLOCK_MONOTONIC, &a);
+        orc_moe_layer(M, H, I, E, K, x, wr, w13, s13, w2, sc2, logits, ids, w, gap, q, s, h, q2, s2, out);
+        clock_gettime(CLOCK_MONOTONIC, &b);
+        seconds[r] = (double)(b.tv_sec - a.tv_sec) + 1e-9 * (double)(b.tv_nsec - a.tv_nsec);
+    }
 }
 
 /* ------------------------------------------------------------------------- */

@@ -190,3 +190,38 @@ def test_jit_ling_kernels_preferred(moe, cache_dir):
         assert moe.moe_jit_unload(shp) == 1
     st, info = moe.moe_path_info(shp, 1)
     assert st == 0 and "compiled at run time" not in info
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_jit_one_token_items_beyond_the_grid(moe, cache_dir, shared):
+    """One token routed from its logits where the gate/up items outnumber the
+    512-workgroup grid (hidden 2560, intermediate 1088: 68 items per expert,
+    8 x 68 = 544 items, 612 with the shared expert), so that workgroups also
+    take an item of a higher-ranked slot than their first: the whole layer
+    against the oracle (P5) and its routing (P2)."""
+    Hj, Ij, Ej, Kj = 2560, 1088, 16, 8
+    shp = moe.shape(Hj, Ij, Ej, Kj)
+    moe.moe_jit_load(shp, cache_dir)
+    try:
+        w = synth.expert_weights(980, Hj, Ij, Ej)
+        dw = DevWeights(w)
+        ws = moe.workspace(shp, 1)
+        sh = synth.shared_expert(981, Hj, Ij) if shared else None
+        for seed in (982, 983, 984):
+            li = synth.decode_tokens(seed, w, 1, K=Kj)
+            t = oracle.moe_layer(li.x, w.wr, w.w13, w.s13, w.w2, w.s2, Kj,
+                                 shared=oracle.SharedExpert(*sh) if shared else None)
+            if t.flags.any():
+                continue
+            out = torch.empty((1, Hj), dtype=torch.float32, device="cuda")
+            if shared:
+                moe.moe_decode_forward_shared(shp, 1, dev(li.x), dw.wr, dw.w13, dw.s13, dw.w2, dw.s2,
+                                              tuple(dev(a) for a in sh), out, ws)
+            else:
+                moe.moe_decode_forward(shp, 1, dev(li.x), dw.wr, dw.w13, dw.s13, dw.w2, dw.s2, out, ws)
+            torch.cuda.synchronize()
+            err = rel_l2(host(out), t.out)
+            print(f"one token, {Ij}-wide experts, shared={shared}, seed {seed}: rel_l2 {err:.2e}", flush=True)
+            assert err <= 1e-2, err
+    finally:
+        assert moe.moe_jit_unload(shp) == 1
