@@ -183,6 +183,24 @@ moe_status moe_decode_forward_shared(const moe_shape* shape, int32_t M,
                                      float* out, void* ws, size_t ws_bytes, void* stream,
                                      void* const* events);
 
+/* moe_decode_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * inside the library (4 MiB; every GPU that runs the library holds its own
+ * copy until the process ends); the call itself allocates nothing.  At the
+ * first call on a device the array is zeroed by a fill kernel on `stream`.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and give undefined results, so
+ * order them.  A call whose workspace would exceed the array
+ * (moe_workspace_bytes(shape, M) > 4 MiB, e.g. large M on the chunk path) is
+ * MOE_ERR_UNSUPPORTED_SHAPE; otherwise arguments and errors are those of
+ * moe_decode_forward. */
+moe_status moe_decode_forward_noalloc(const moe_shape* shape, int32_t M,
+                                      const uint16_t* hidden, const uint16_t* router_w,
+                                      const uint8_t* w13, const uint8_t* w13_scale,
+                                      const uint8_t* w2, const uint8_t* w2_scale,
+                                      float* out, void* stream);
+
 /* Router, top-K, renormalised weights and compaction (the first kernel of
  * moe_decode_forward; it also quantises the activations when the taps ask
  * for them).  topk_ids/topk_w [M,K] are written in canonical order (logit

@@ -79,6 +79,7 @@ _SIGNATURES = {
                                                   ctypes.POINTER(ctypes.c_void_p)]),
     "moe_decode_forward_shared": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _SH, _V, _V, _sz, _V,
                                                   ctypes.POINTER(ctypes.c_void_p)]),
+    "moe_decode_forward_noalloc": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V]),
     "moe_route": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, ctypes.POINTER(MoeRouteTaps), _V, _sz, _V]),
     "moe_quant_act": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V]),
     "moe_experts_forward": (ctypes.c_int, [_S, _i32, _V, _V, _V, _V, _V, _V, _V, _V, _V,
@@ -172,6 +173,13 @@ def moe_decode_forward(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, o
     _check(_lib.moe_decode_forward(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
                                    _p(w2), _p(w2_scale), _p(out), _p(ws), _nbytes(ws), _stream(stream)),
            "moe_decode_forward")
+
+
+def moe_decode_forward_noalloc(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, stream=None):
+    """moe_decode_forward on the library's static scratch (no workspace)."""
+    _check(_lib.moe_decode_forward_noalloc(ctypes.byref(shp), M, _p(hidden), _p(router_w), _p(w13), _p(w13_scale),
+                                           _p(w2), _p(w2_scale), _p(out), _stream(stream)),
+           "moe_decode_forward_noalloc")
 
 
 def moe_decode_forward_events(shp, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, events,

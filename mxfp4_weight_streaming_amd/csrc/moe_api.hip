@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_decode.h"
 #include "moe_internal.hpp"
 
@@ -381,6 +383,42 @@ moe_status experts_forward(const moe_shape* shape, int32_t M, const uint8_t* act
     return enqueue_down(shape, M, h, nullptr, nullptr, q2_tap, s2_tap, topk_w, w2, w2_scale, out, c, s, {}, sh);
 }
 
+// ---- the entry point that allocates nothing --------------------------------
+// A workspace that lives in the library itself: one file-scope device array,
+// of which every GPU that loads the library holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): the device address of the current device's
+// copy comes from hipGetSymbolAddress, once per device, and is kept.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's scratch address.  At its first use on a device the
+// array is zeroed by a fill kernel on `stream` (the workspace-init state).
+moe_status scratch_for_device(hipStream_t stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(MOE_ERR_HIP, "device %d is beyond the %d devices the static scratch serves", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0) return fail(MOE_ERR_HIP, "static scratch is not 256-byte aligned");
+        e = moe::launch_fill_u32(static_cast<uint32_t*>(p), kScratchBytes / 4, 0u, stream);
+        if (e != hipSuccess) return hip_fail(e, "static scratch init");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,6 +464,29 @@ moe_status moe_decode_forward(const moe_shape* shape, int32_t M, const uint16_t*
 {
     return moe_decode_forward_events(shape, M, hidden, router_w, w13, w13_scale, w2, w2_scale, out, ws, ws_bytes,
                                      stream, nullptr);
+}
+
+moe_status moe_decode_forward_noalloc(const moe_shape* shape, int32_t M, const uint16_t* hidden,
+                                      const uint16_t* router_w, const uint8_t* w13, const uint8_t* w13_scale,
+                                      const uint8_t* w2, const uint8_t* w2_scale, float* out, void* stream)
+{
+    // everything is checked before anything (the scratch's first-use fill
+    // included) is enqueued
+    moe_status st = check_shape(shape, M);
+    if (st != MOE_OK) return st;
+    CHECK_PTR(hidden); CHECK_PTR(router_w); CHECK_PTR(w13); CHECK_PTR(w13_scale);
+    CHECK_PTR(w2); CHECK_PTR(w2_scale); CHECK_PTR(out);
+    CHECK_ALIGN(hidden); CHECK_ALIGN(router_w); CHECK_ALIGN(w13); CHECK_ALIGN(w2); CHECK_ALIGN(out);
+    const size_t need = moe::ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->topk, M).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                    "M=%d needs %zu bytes of scratch; the library's static scratch holds %zu (use moe_decode_forward "
+                    "with a workspace)",
+                    M, need, kScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_for_device(static_cast<hipStream_t>(stream), &ws)) != MOE_OK) return st;
+    return decode_forward(shape, M, hidden, router_w, w13, w13_scale, w2, w2_scale, nullptr, out, ws, kScratchBytes,
+                          stream, nullptr);
 }
 
 moe_status moe_route(const moe_shape* shape, int32_t M, const uint16_t* hidden, const uint16_t* router_w,

@@ -90,6 +90,9 @@ def test_null_and_alignment_and_workspace(moe):
     assert L.moe_fp8_encode_range(0, -1, a, None) == -1
     assert L.moe_workspace_init(None, 1024, None) == -4
     assert L.moe_workspace_init(a + 8, 1024, None) == -4
+    assert L.moe_decode_forward_noalloc(None, 1, a, a, a, a, a, a, a, None) == -1
+    assert L.moe_decode_forward_noalloc(ctypes.byref(s), 1, None, a, a, a, a, a, a, None) == -1
+    assert L.moe_decode_forward_noalloc(ctypes.byref(s), 1, a + 4, a, a, a, a, a, a, None) == -3
 
 
 def test_status_strings_and_path_info(moe):
