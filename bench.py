@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--lm-head-steps", type=int, default=400, help="timed LM-head GEMV calls per token count")
     p.add_argument("--shared-steps", type=int, default=4000,
                    help="layer forwards timed again with a shared expert per layer (0: skip)")
+    p.add_argument("--one-kernel", action="store_true",
+                   help="time the one-kernel M <= 8 layer (layer_kernel) instead of the default three kernels")
     return p.parse_args()
 
 
@@ -112,6 +114,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"reference copy: {args.copy_mb} MiB x 3")
         del src, dst
+    if args.one_kernel:
+        moe.moe_set_decode_path(moe.PATH_ONE_KERNEL)
     shp = moe.shape(H, I, E, K)
     L, reps = args.layers, args.reps
     st, path = moe.moe_path_info(shp, 1)
@@ -313,9 +317,10 @@ def time_walks(args, moe, synth, stack, shared_layers, shp, stream, ws, out, nam
     # head of the stream lets the host queue the whole walk first, so the
     # kernels run back to back as in the timed walk)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
-    names = ("router", "gate_up", "down")
+    one_kernel = "one-kernel" in moe.moe_path_info(shp, M)[1]
+    names = ("layer",) if one_kernel else ("router", "gate_up", "down")
     dur = {k: [] for k in names}
-    gu_launch_bytes = []
+    gu_launch_bytes, layer_launch_bytes = [], []
     with torch.cuda.stream(stream):
         for row in evs:
             for e in row:
@@ -330,6 +335,7 @@ def time_walks(args, moe, synth, stack, shared_layers, shp, stream, ws, out, nam
                 for k, kn in enumerate(names):
                     dur[kn].append(evs[l][2 * k].elapsed_time(evs[l][2 * k + 1]))
                 gu_launch_bytes.append(int(n_act[r, l]) * W13_BYTES)
+                layer_launch_bytes.append(lb[r][l])
     kus = {k: float(np.mean(v)) * 1e3 for k, v in dur.items()}
     gu_bytes = float(np.mean(gu_launch_bytes))
     log(f"{name}: kernel means (us) {kus}")
@@ -366,15 +372,23 @@ def time_walks(args, moe, synth, stack, shared_layers, shp, stream, ws, out, nam
         log(f"{name} with a shared expert: {shared['us_per_layer']:.2f} us/layer, {shared['gbs']:.0f} GB/s")
         del gsh
     del graphs, prefix
+    errs = moe.sync_errors(ws)
+    if errs:
+        raise RuntimeError(f"{name}: the layer kernel's waits ran out (sync error bits {errs:#x}); results invalid")
     return {"us_per_layer": ms * 1e3 / steps, "gbs": gbs, "steps": steps, "ms": ms,
             "per_set": {"median": round(float(np.median(per_set)), 3), "min": round(min(per_set), 3),
                         "max": round(max(per_set), 3), "sets": reps},
             "mean_distinct_experts": float(n_act.mean()),
             "plain_us_per_layer": pms * 1e3 / n_plain, "plain_gbs": pbytes / (pms * 1e-3) / 1e9,
             "kernel_us": kus, "shared": shared,
-            "roofline": {"kernel": f"gate_up_kernel<H=2560,I=768> ({M} token(s))", "bytes": gu_bytes,
-                         "us": kus["gate_up"], "gbs": gu_bytes / (kus["gate_up"] * 1e-6) / 1e9,
-                         "timing": "launch-stamped HIP events, plain launches queued behind a spin kernel"}}
+            "roofline": ({"kernel": f"layer_kernel<H=2560,I=768> ({M} token(s), the whole layer)",
+                          "bytes": float(np.mean(layer_launch_bytes)), "us": kus["layer"],
+                          "gbs": float(np.mean(layer_launch_bytes)) / (kus["layer"] * 1e-6) / 1e9,
+                          "timing": "launch-stamped HIP events, plain launches queued behind a spin kernel"}
+                         if one_kernel else
+                         {"kernel": f"gate_up_kernel<H=2560,I=768> ({M} token(s))", "bytes": gu_bytes,
+                          "us": kus["gate_up"], "gbs": gu_bytes / (kus["gate_up"] * 1e-6) / 1e9,
+                          "timing": "launch-stamped HIP events, plain launches queued behind a spin kernel"})}
 
 
 def lm_head_bench(args, moe, stream) -> dict:

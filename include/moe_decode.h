@@ -72,10 +72,13 @@
  * kernels a call would run so that callers can check at startup that the path
  * they expect is active, as the pages advise.  Non-finite inputs are not
  * detected; results for them are unspecified.  Caller-given topk_ids must
- * lie in [0, E) and, for M <= 8, be distinct within a token.  For M > 8 a
- * token may also name one expert more than once: each (token, j) pair is then
- * computed and weighted on its own.  Other ids give unspecified results (they
- * are clamped on the device, never read or written out of bounds).
+ * lie in [0, E).  A token may name one expert more than once on the chunk
+ * path (M > 8) and on the one-kernel path (moe_experts_forward at M <= 8
+ * with MOE_PATH_ONE_KERNEL selected): each (token, j) pair is then computed
+ * and weighted on its own.  On the three-kernel M <= 8 path and in
+ * moe_gate_up / moe_down_combine at M <= 8 the ids of a token must be
+ * distinct.  Other ids give unspecified results (they are clamped on the
+ * device, never read or written out of bounds).
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
@@ -141,14 +144,56 @@ typedef struct {
  * every smaller M, with or without a shared expert. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_tokens);
 
+/* How M <= 8 runs (chunk-path calls, M > 8, are not affected).
+ * MOE_PATH_THREE_KERNELS (the default): router, gate/up and down kernels in
+ * stream order.  MOE_PATH_ONE_KERNEL: the whole layer as one kernel
+ * (layer_kernel) with one workgroup per compute unit, whose workgroups hand
+ * logits, intermediate rows and down outputs to each other through
+ * epoch-tagged words in the workspace instead of kernel boundaries; shapes
+ * outside its LDS plan keep the three kernels.  At Ling-3.0-flash's shape on
+ * MI355X the one-kernel layer measures slower (the hand-offs cost more under
+ * 256-way polling than a kernel boundary), so it is opt-in. */
+typedef enum {
+    MOE_PATH_THREE_KERNELS = 0,
+    MOE_PATH_ONE_KERNEL = 1
+} moe_decode_path;
+
+/* Selects the M <= 8 path for later calls from any thread (a process-wide
+ * setting, like moe_set_wait_limit_us).  MOE_ERR_INVALID_ARG for any other
+ * value.  moe_path_info reports the selection. */
+moe_status moe_set_decode_path(int32_t path);
+
 /* Zero the workspace (a fill kernel on `stream`; the caller orders later
- * calls on other streams after it).  No call depends on what an earlier call
- * left in the workspace, so this is optional; it makes a workspace that was
- * never written read as "no expert selected".  ws must be 256-byte aligned. */
+ * calls on other streams after it).  Required once for a new workspace before
+ * its first call: on the one-kernel path the layer's workgroups hand results
+ * to each other through epoch-tagged words kept at the start of the
+ * workspace, and the epoch carries over from call to call (zeroing again
+ * later is allowed; it clears the sticky wait-error bits as well).  ws must
+ * be 256-byte aligned. */
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
+/* Copies (on `stream`, device to device) the workspace's sticky wait-error
+ * bits into *status, a caller device word: 0 when every call of the one-kernel
+ * layer since moe_workspace_init completed its hand-offs.  The layer kernel's
+ * workgroups wait for each other (they are all resident at once: one per
+ * compute unit); every such wait is bounded (0.2 s by default), and a wait
+ * that runs out sets bit 1 (router logits), 2 (intermediate rows), 4 (down
+ * outputs) or 8 (arrivals) and lets the kernel finish with an undefined
+ * result.  A wait can only run out when another kernel occupies compute units
+ * for longer than the bound, e.g. more than one of these layers running
+ * concurrently on one GPU. */
+moe_status moe_workspace_sync_status(const void* ws, size_t ws_bytes, uint32_t* status, void* stream);
+
+/* Sets the bound of every wait of the one-kernel layer, in microseconds, for
+ * later launches from any thread (0 restores the default, 0.2 s).  For tests
+ * of the wait-error path. */
+void moe_set_wait_limit_us(uint32_t us);
+
 /* The whole layer for M tokens: route -> quantise -> compact -> gate/up ->
- * requantise -> down + combine.  out[M,H] fp32 is overwritten. */
+ * requantise -> down + combine.  out[M,H] fp32 is overwritten.  M <= 8 runs
+ * as three kernels (router, gate/up, down), or as one (layer_kernel) when
+ * moe_set_decode_path selected it and its LDS plan fits; M > 8 runs the chunk
+ * path.  moe_path_info names the kernels. */
 moe_status moe_decode_forward(const moe_shape* shape, int32_t M,
                               const uint16_t* hidden, const uint16_t* router_w,
                               const uint8_t* w13, const uint8_t* w13_scale,
@@ -157,7 +202,8 @@ moe_status moe_decode_forward(const moe_shape* shape, int32_t M,
 
 /* moe_decode_forward with per-kernel timing: `events` is an array of 6
  * caller-created hipEvent_t (timing enabled), start/stop pairs for the router
- * (0, 1), gate/up (2, 3) and down (4, 5) kernels.  Each pair is stamped by the
+ * (0, 1), gate/up (2, 3) and down (4, 5) kernels; on the one-kernel path the
+ * pair (0, 1) times layer_kernel and the other events are not used.  Each pair is stamped by the
  * kernel's own launch (hipExtLaunchKernel), so hipEventElapsedTime of a pair
  * is that kernel's execution time on the GPU, without queueing or dispatch
  * gaps.  `events` may be NULL (then this is moe_decode_forward); a NULL pair

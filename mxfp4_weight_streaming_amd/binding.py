@@ -95,6 +95,9 @@ _SIGNATURES = {
     "moe_jit_build": (ctypes.c_int, [_S, ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(MoeJitReport)]),
     "moe_jit_load": (ctypes.c_int, [_S, ctypes.c_char_p, _i32, ctypes.POINTER(MoeJitReport)]),
     "moe_jit_unload": (_i32, [_S]),
+    "moe_workspace_sync_status": (ctypes.c_int, [_V, _sz, _V, _V]),
+    "moe_set_wait_limit_us": (None, [ctypes.c_uint32]),
+    "moe_set_decode_path": (ctypes.c_int, [_i32]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -323,6 +326,35 @@ def moe_path_info(shp: MoeShape, M: int) -> tuple[int, str]:
     buf = ctypes.create_string_buffer(1024)
     st = _lib.moe_path_info(ctypes.byref(shp), M, buf, len(buf))
     return st, buf.value.decode()
+
+
+def moe_workspace_sync_status(ws, status, stream=None) -> None:
+    """Copy the workspace's sticky wait-error bits into `status` (a device
+    int32/uint32 tensor of one element)."""
+    _check(_lib.moe_workspace_sync_status(_p(ws), _nbytes(ws), _p(status), _stream(stream)),
+           "moe_workspace_sync_status")
+
+
+def sync_errors(ws) -> int:
+    """The workspace's wait-error bits, read back (synchronises the current stream)."""
+    import torch
+    st = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    moe_workspace_sync_status(ws, st)
+    return int(st.item())
+
+
+def moe_set_wait_limit_us(us: int) -> None:
+    _lib.moe_set_wait_limit_us(us)
+
+
+PATH_THREE_KERNELS = 0
+PATH_ONE_KERNEL = 1
+
+
+def moe_set_decode_path(path: int) -> None:
+    """Select how M <= 8 runs for later calls: PATH_THREE_KERNELS (default) or
+    PATH_ONE_KERNEL (layer_kernel)."""
+    _check(_lib.moe_set_decode_path(path), "moe_set_decode_path")
 
 
 def moe_status_string(status: int) -> str:

@@ -136,7 +136,7 @@ __device__ void compact_wave(int P, int K, RouteLds& r)
 // Compaction of the ids in r.ids (and the shared expert's slot), by wave 0;
 // the caller synchronises before and after.  distinct: the ids of the one
 // token are known to be distinct (routed by top-K), which takes a fast path.
-__device__ void route_compact(int M, int K, bool distinct, int shared, RouteLds& r)
+__device__ __forceinline__ void route_compact(int M, int K, bool distinct, int shared, RouteLds& r)
 {
     const int tid = threadIdx.x, P = M * K;
     if ((tid >> 6) != 0) return;

@@ -110,6 +110,7 @@ std::vector<KernelKey> module_keys(int H, int I, bool chunk, bool lm)
         keys.push_back(key_gate_up(H, I, mt));
         keys.push_back(key_down(H, I, mt, true));
         keys.push_back(key_down(H, I, mt, false));
+        if (layer_shape_ok(H, I)) keys.push_back(key_layer(H, I, mt));
     }
     if (chunk) {
         keys.push_back(key_chunk_router(H));
@@ -125,7 +126,7 @@ std::vector<KernelKey> module_keys(int H, int I, bool chunk, bool lm)
 
 std::string main_source(bool chunk, bool lm)
 {
-    std::string s = "#include \"gemv_kernels.hpp\"\n";
+    std::string s = "#include \"gemv_kernels.hpp\"\n#include \"layer_kernels.hpp\"\n";
     if (chunk) s += "#include \"chunk_kernels.hpp\"\n";
     if (lm) s += "#include \"lm_head_kernels.hpp\"\n";
     return s;
@@ -404,6 +405,7 @@ bool kernel_expr(const KernelKey& k, char* buf, size_t n)
             return true;
         case KernelKind::Combine: snprintf(buf, n, "moe::combine_kernel<%d>", k.H); return true;
         case KernelKind::LmHead: snprintf(buf, n, "moe::lm_head_gemv_kernel<%d, %d>", k.H, k.v); return true;
+        case KernelKind::Layer: snprintf(buf, n, "moe::layer_kernel<%d, %d, %d>", k.H, k.I, k.v); return true;
     }
     return false;
 }

@@ -23,6 +23,7 @@ enum class KernelKind : int {
     ChunkDown,    // chunk_down_kernel<H, I, BY_PAIR>        v = BY_PAIR
     Combine,      // combine_kernel<H>
     LmHead,       // lm_head_gemv_kernel<H, MT>              v = MT
+    Layer,        // layer_kernel<H, I, MT>                  v = MT
 };
 
 // H or I is 0 for a kernel templated on the other one only.
@@ -46,6 +47,7 @@ inline KernelKey key_chunk_gate_up(int H, int I) { return {KernelKind::ChunkGate
 inline KernelKey key_chunk_down(int H, int I, bool by_pair) { return {KernelKind::ChunkDown, H, I, by_pair ? 1 : 0}; }
 inline KernelKey key_combine(int H) { return {KernelKind::Combine, H, 0, 0}; }
 inline KernelKey key_lm_head(int H, int mt) { return {KernelKind::LmHead, H, 0, mt}; }
+inline KernelKey key_layer(int H, int I, int mt) { return {KernelKind::Layer, H, I, mt}; }
 
 // The kernel's qualified template-id, e.g. "moe::gate_up_kernel<2560, 768, 1>"
 // (the name expression hipRTC resolves).  Returns false for an unknown kind.

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "moe_decode.h"
@@ -116,6 +117,11 @@ struct Carved {
     moe::ChunkList chunks(const moe_shape* s, int32_t M, bool shared) const
     {
         return {at<int32_t>(L.n_chunks), at<int4>(L.chunk_rec), chunk_cap(s, M, shared)};
+    }
+    moe::LayerSync sync() const
+    {
+        return {at<uint32_t>(L.sync_word), at<uint32_t>(L.sync_epochs), at<uint64_t>(L.sync_arrive),
+                at<uint64_t>(L.sync_logits), at<uint64_t>(L.sync_h), at<uint64_t>(L.sync_y)};
     }
 };
 
@@ -284,6 +290,39 @@ moe_status enqueue_chunk_experts(const moe_shape* s, int32_t M, const uint8_t* a
     return enqueue_combine(s, M, topk_w, out, c, st, has_shared(sh));
 }
 
+// The M <= 8 path chosen by moe_set_decode_path (three kernels by default).
+std::atomic<int32_t> g_decode_path{MOE_PATH_THREE_KERNELS};
+
+// M <= 8 runs as one kernel when that path is selected, its kernels exist for
+// (H, I) and its LDS plan fits; otherwise as the three kernels router ->
+// gate/up -> down.  moe_path_info names the choice.
+bool use_layer(const moe_shape* s, int32_t M, bool shared)
+{
+    if (g_decode_path.load(std::memory_order_relaxed) != MOE_PATH_ONE_KERNEL) return false;
+    if (chunked(M) || !moe::layer_shape_supported(s->hidden, s->inter)) return false;
+    const int pe = M * s->topk + (shared ? M : 0);
+    return moe::layer_lds_bytes(s->hidden, s->inter, token_bound(M), pe) <= moe::kLayerMaxDynLds;
+}
+
+moe::LayerArgs layer_args(const moe_shape* s, int32_t M, const uint8_t* w13, const uint8_t* w13_scale,
+                          const uint8_t* w2, const uint8_t* w2_scale, const moe::SharedWeights& sh, float* out,
+                          const Carved& c)
+{
+    moe::LayerArgs a{};
+    a.M = M;
+    a.E = s->num_experts;
+    a.K = s->topk;
+    a.shared = has_shared(sh) ? 1 : 0;
+    a.w13 = w13;
+    a.s13 = w13_scale;
+    a.w2 = w2;
+    a.sw2 = w2_scale;
+    a.sh = sh;
+    a.out = out;
+    a.sync = c.sync();
+    return a;
+}
+
 // A shared expert's four tensors: all given, 16-byte aligned codes.
 moe_status check_shared(const moe_shared_expert* sh)
 {
@@ -326,6 +365,13 @@ moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hid
     uint8_t* q = c.at<uint8_t>(c.L.act_q);
     float* sc = c.at<float>(c.L.act_s);
     float* h = c.at<float>(c.L.h);
+    if (use_layer(shape, M, has_shared(sh))) {
+        moe::LayerArgs a = layer_args(shape, M, w13, w13_scale, w2, w2_scale, sh, out, c);
+        a.x = hidden;
+        a.wr = router_w;
+        hipError_t e = moe::launch_layer(shape->hidden, shape->inter, token_bound(M), a, s, ev(0));
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "layer launch");
+    }
     if (chunked(M)) {
         if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s, ev(0))) != MOE_OK) return st;
         if ((st = enqueue_quant(shape, M, hidden, q, sc, s)) != MOE_OK) return st;
@@ -373,6 +419,20 @@ moe_status experts_forward(const moe_shape* shape, int32_t M, const uint8_t* act
         if ((st = gather_out(taps->h, c.at<void>(c.L.h), R, I * 4, c, s)) != MOE_OK) return st;
         if ((st = gather_out(taps->inter_fp8, c.at<void>(c.L.q2), R, I, c, s)) != MOE_OK) return st;
         return gather_out(taps->inter_scale, c.at<void>(c.L.s2), R, 4, c, s);
+    }
+    if (use_layer(shape, M, has_shared(sh))) {
+        moe::LayerArgs a = layer_args(shape, M, w13, w13_scale, w2, w2_scale, sh, out, c);
+        a.act_q = act_fp8;
+        a.act_s = act_scale;
+        a.ids = topk_ids;
+        a.topk_w = topk_w;
+        if (taps != nullptr) {
+            a.h_tap = taps->h;
+            a.q2_tap = taps->inter_fp8;
+            a.s2_tap = taps->inter_scale;
+        }
+        hipError_t e = moe::launch_layer(shape->hidden, shape->inter, token_bound(M), a, s);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "layer launch");
     }
     float* h = (taps && taps->h) ? taps->h : c.at<float>(c.L.h);
     uint8_t* q2_tap = taps ? taps->inter_fp8 : nullptr;
@@ -652,6 +712,10 @@ moe_status moe_path_info(const moe_shape* shape, int32_t M, char* buf, size_t le
         } else if (chunked(M)) {
             moe::chunk_kernel_names(shape->hidden, shape->inter, names, sizeof names);
             snprintf(buf, len, "chunk path, M=%d, E=%d, K=%d: %s", M, shape->num_experts, shape->topk, names);
+        } else if (use_layer(shape, M, false)) {
+            moe::layer_kernel_names(shape->hidden, shape->inter, names, sizeof names);
+            snprintf(buf, len, "one-kernel gemv path, M=%d (token bound %d), E=%d, K=%d: %s", M, token_bound(M),
+                     shape->num_experts, shape->topk, names);
         } else {
             moe::kernel_names(shape->hidden, shape->inter, names, sizeof names);
             snprintf(buf, len, "gemv path, M=%d (token bound %d), E=%d, K=%d: %s", M, token_bound(M),
@@ -727,5 +791,26 @@ const char* moe_status_string(moe_status status)
 }
 
 const char* moe_last_error(void) { return g_last_error; }
+
+moe_status moe_workspace_sync_status(const void* ws, size_t ws_bytes, uint32_t* status, void* stream)
+{
+    if (ws == nullptr || ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace is NULL or below 256 bytes");
+    if (((uintptr_t)ws & 255u) != 0) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (status == nullptr) return fail(MOE_ERR_INVALID_ARG, "status is NULL");
+    // the error word follows the epoch at the start of the workspace
+    hipError_t e = hipMemcpyAsync(status, static_cast<const uint32_t*>(ws) + 1, 4, hipMemcpyDeviceToDevice,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "sync status copy");
+}
+
+void moe_set_wait_limit_us(uint32_t us) { moe::set_layer_wait_us(us); }
+
+moe_status moe_set_decode_path(int32_t path)
+{
+    if (path != MOE_PATH_THREE_KERNELS && path != MOE_PATH_ONE_KERNEL)
+        return fail(MOE_ERR_INVALID_ARG, "decode path %d is neither 0 (three kernels) nor 1 (one kernel)", path);
+    g_decode_path.store(path, std::memory_order_relaxed);
+    return MOE_OK;
+}
 
 }  // extern "C"

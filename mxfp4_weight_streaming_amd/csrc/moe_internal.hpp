@@ -16,10 +16,18 @@ namespace moe {
 
 // Dynamic LDS a kernel may take on gfx950 (160 KiB per compute unit).
 constexpr size_t kMaxDynamicLds = 160 * 1024;
+// The layer kernel: at least this much LDS, so that a compute unit holds one
+// of its workgroups; at most what leaves room for its static LDS.
+constexpr size_t kLayerMinLds = 84 * 1024;
+constexpr size_t kLayerMaxDynLds = 152 * 1024;
 
-// Workspace carving.  No state is carried between calls: every call writes
-// what it later reads.  pos_of and y exist only for the chunk path.
+// Workspace carving.  The one-kernel layer's hand-off region (LayerSync)
+// comes first and its layout does not depend on M: its epoch and tags carry
+// over from call to call (moe_workspace_init zeroes them once).  Everything
+// after it is written by a call before that call reads it.  pos_of and y
+// exist only for the chunk path.
 struct WsLayout {
+    size_t sync_word, sync_epochs, sync_arrive, sync_logits, sync_h, sync_y;
     size_t logits, ids, w, act_q, act_s, n_act, act_experts, offsets, pair_token, pair_src, h, q2, s2, pos_of, y,
         n_chunks, chunk_rec, total;
 };
@@ -35,6 +43,12 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int M)
     const size_t S = (size_t)(E < (int)P ? E : (int)P) + 1;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    L.sync_word = take(256);
+    L.sync_epochs = take((size_t)kMaxLayerBlocks * 4);
+    L.sync_arrive = take((size_t)kMaxLayerBlocks * 8);
+    L.sync_logits = take((size_t)kMaxGemvTokens * E * 8);
+    L.sync_h = take((size_t)kMaxPairsExt * I * 8);
+    L.sync_y = take((size_t)kMaxPairsExt * H * 8);
     L.logits = take((size_t)M * E * 4);
     L.ids = take(P * 4);
     L.w = take(P * 4);
@@ -77,10 +91,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_gate_up(int H, int I, int mt, int S, const GateUpArgs& a, hipStream_t s,
                           const LaunchEvents& ev = {});  // S: slot bound
 hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, const LaunchEvents& ev = {});
+// The one-kernel layer (M <= 8); a.wait_ticks is filled in here when zero.
+bool layer_shape_supported(int H, int I);
+hipError_t launch_layer(int H, int I, int mt, LayerArgs a, hipStream_t s, const LaunchEvents& ev = {});
+// Bound of the layer kernel's waits, in microseconds (0: the default).
+void set_layer_wait_us(uint32_t us);
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* q, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 void kernel_names(int H, int I, char* buf, size_t n);
+void layer_kernel_names(int H, int I, char* buf, size_t n);
 
 // Chunk-path launchers (moe_chunk.hip).
 bool chunk_shape_supported(int H, int I, int E);

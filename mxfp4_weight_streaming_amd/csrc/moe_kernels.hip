@@ -4,7 +4,12 @@
 #include <hip/hip_ext.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+
 #include "gemv_kernels.hpp"
+#include "layer_kernels.hpp"
 #include "kernel_table.hpp"
 #include "moe_internal.hpp"
 
@@ -19,14 +24,17 @@ namespace moe {
     {key_gate_up(H, I, MT), (const void*)gate_up_kernel<H, I, MT>},                             \
     {key_down(H, I, MT, true), (const void*)down_kernel<H, I, MT, true>},                       \
     {key_down(H, I, MT, false), (const void*)down_kernel<H, I, MT, false>},
+#define MOE_LAYER_MT(H, I, MT) {key_layer(H, I, MT), (const void*)layer_kernel<H, I, MT>},
 #define MOE_GEMV_SHAPE(H, I)                                                                     \
     {key_quant(H), (const void*)quant_kernel<H>}, {key_requant(I), (const void*)requant_kernel<I>}, \
-    MOE_GEMV_MT(H, I, 1) MOE_GEMV_MT(H, I, 2) MOE_GEMV_MT(H, I, 4) MOE_GEMV_MT(H, I, 8)
+    MOE_GEMV_MT(H, I, 1) MOE_GEMV_MT(H, I, 2) MOE_GEMV_MT(H, I, 4) MOE_GEMV_MT(H, I, 8)          \
+    MOE_LAYER_MT(H, I, 1) MOE_LAYER_MT(H, I, 2) MOE_LAYER_MT(H, I, 4) MOE_LAYER_MT(H, I, 8)
 
 const AotKernel kGemvAot[] = {MOE_GEMV_SHAPE(256, 64) MOE_GEMV_SHAPE(2560, 768)};
 const int kGemvAotCount = (int)(sizeof(kGemvAot) / sizeof(kGemvAot[0]));
 #undef MOE_GEMV_SHAPE
 #undef MOE_GEMV_MT
+#undef MOE_LAYER_MT
 
 // The decode path has kernels for (H, I): compiled in, or loaded at run time.
 bool gemv_shape_supported(int H, int I)
@@ -83,6 +91,72 @@ hipError_t launch_down(int H, int I, int mt, const DownArgs& a, hipStream_t s, c
     return launch_kern(k, dim3(H / down_rows_per_block(H, I)), dim3(512), (uint32_t)lds, s, ev, a);
 }
 
+// ---------------------------------------------------------------------------
+// The one-kernel layer.
+// ---------------------------------------------------------------------------
+bool layer_shape_supported(int H, int I)
+{
+    return layer_shape_ok(H, I) && find_kernel(key_layer(H, I, 1)).ok();
+}
+
+namespace {
+std::atomic<uint32_t> g_layer_wait_us{0};
+constexpr uint32_t kDefaultLayerWaitUs = 200000;   // 0.2 s: far above any real wait
+
+struct DeviceFacts {
+    int cus = 0;
+    uint64_t wall_khz = 0;
+};
+std::mutex g_facts_mu;
+DeviceFacts g_facts[64];
+
+hipError_t device_facts(DeviceFacts* out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_facts_mu);
+    DeviceFacts& f = g_facts[dev];
+    if (f.cus == 0) {
+        int cus = 0, khz = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+        f.wall_khz = khz > 0 ? (uint64_t)khz : 100000;
+        f.cus = cus > 0 ? cus : 1;
+    }
+    *out = f;
+    return hipSuccess;
+}
+}  // namespace
+
+void set_layer_wait_us(uint32_t us) { g_layer_wait_us.store(us); }
+
+hipError_t launch_layer(int H, int I, int mt, LayerArgs a, hipStream_t s, const LaunchEvents& ev)
+{
+    const Kern k = find_kernel(key_layer(H, I, mt));
+    if (!k.ok()) return hipErrorInvalidDeviceFunction;
+    DeviceFacts d;
+    hipError_t e = device_facts(&d);
+    if (e != hipSuccess) return e;
+    const uint32_t us = g_layer_wait_us.load();
+    if (a.wait_ticks == 0) a.wait_ticks = (uint64_t)(us ? us : kDefaultLayerWaitUs) * d.wall_khz / 1000u;
+    // one workgroup per compute unit (all resident at once: the workgroups
+    // wait for each other), and no more than the work has tasks for
+    const int slots = std::min(a.E, a.M * a.K) + (a.shared ? 1 : 0);
+    const int need = std::max({slots * layer_gate_up_tasks(H, I), slots * layer_down_tasks(H, I), a.E, 1});
+    const int nb = std::min({d.cus, need, kMaxLayerBlocks});
+    // the LDS request keeps one workgroup per compute unit
+    const int pe = a.M * a.K + (a.shared ? a.M : 0);
+    const size_t lds = std::max(layer_lds_bytes(H, I, mt, pe), kLayerMinLds);
+    if (lds > kLayerMaxDynLds) return hipErrorInvalidValue;
+    if (lds > 64 * 1024 && k.aot != nullptr) {
+        e = hipFuncSetAttribute(k.aot, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    return launch_kern(k, dim3(nb), dim3(512), (uint32_t)lds, s, ev, a);
+}
+
 hipError_t launch_requant(int I, const RequantArgs& a, hipStream_t s)
 {
     if (a.P <= 0) return hipSuccess;
@@ -106,6 +180,19 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s)
     const size_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
+}
+
+void layer_kernel_names(int H, int I, char* buf, size_t n)
+{
+    const Kern k = find_kernel(key_layer(H, I, 1));
+    DeviceFacts d;
+    const int cus = device_facts(&d) == hipSuccess ? d.cus : 0;
+    snprintf(buf, n,
+             "layer_kernel<H=%d,I=%d> (one kernel: router, top-K, FP8 quantisation, compaction, gate/up, "
+             "requantisation, down, combine; up to %d workgroups of 512 threads, one per compute unit, handing off "
+             "through epoch-tagged words; gate/up tasks of %d row pairs, down tasks of %d rows)%s",
+             H, I, cus, kWaveSize / gate_up_lanes_per_row(H), layer_down_rows_per_pass(I) * layer_down_passes(H, I),
+             k.jit != nullptr ? " [compiled at run time]" : "");
 }
 
 void kernel_names(int H, int I, char* buf, size_t n)

@@ -184,6 +184,7 @@ struct CombineArgs {
 // zeroed once by moe_workspace_init; its layout does not depend on M.
 struct LayerSync {
     uint32_t* word;        // [0] epoch of the last call, [1] sticky error bits
+    uint32_t* epochs;      // [kMaxLayerBlocks] the epoch again, one copy per workgroup slot
     uint64_t* arrive;      // [kMaxLayerBlocks] one word per workgroup
     uint64_t* logits;      // [kMaxGemvTokens, E]
     uint64_t* h;           // [kMaxPairsExt, I] gate/up output, pair order
@@ -317,6 +318,12 @@ __host__ __device__ constexpr int layer_down_tasks(int H, int I)
     return H / (layer_down_rows_per_pass(I) * layer_down_passes(H, I));
 }
 constexpr int kLayerWaves = 8;
+// Dynamic LDS of the layer kernel: every token's activations as f16, then the
+// FP8 intermediate (as f16) of the nq pairs of a workgroup's down slots.
+__host__ __device__ constexpr size_t layer_lds_bytes(int H, int I, int mt, int nq)
+{
+    return (size_t)mt * H * 2 + (size_t)nq * I * 2;
+}
 // The one-kernel layer exists for (H, I) when its register plan holds: at most
 // 5 gate/up blocks and 6 down blocks per lane and task.
 __host__ __device__ constexpr bool layer_shape_ok(int H, int I)

@@ -90,6 +90,9 @@ def test_null_and_alignment_and_workspace(moe):
     assert L.moe_fp8_encode_range(0, -1, a, None) == -1
     assert L.moe_workspace_init(None, 1024, None) == -4
     assert L.moe_workspace_init(a + 8, 1024, None) == -4
+    assert L.moe_workspace_sync_status(None, 1024, a, None) == -4
+    assert L.moe_workspace_sync_status(a + 8, 1024, a, None) == -4
+    assert L.moe_workspace_sync_status(a, 1024, None, None) == -1
     assert L.moe_decode_forward_noalloc(None, 1, a, a, a, a, a, a, a, None) == -1
     assert L.moe_decode_forward_noalloc(ctypes.byref(s), 1, None, a, a, a, a, a, a, None) == -1
     assert L.moe_decode_forward_noalloc(ctypes.byref(s), 1, a + 4, a, a, a, a, a, a, None) == -3
@@ -99,7 +102,19 @@ def test_status_strings_and_path_info(moe):
     for st in (0, -1, -2, -3, -4, -5):
         assert moe.moe_status_string(st)
     st, info = moe.moe_path_info(_shape(moe), 1)
-    assert st == 0 and "gate_up_kernel<H=2560,I=768>" in info and "down_kernel" in info
+    assert st == 0 and info.startswith("gemv path") and "gate_up_kernel" in info
+    moe.moe_set_decode_path(moe.PATH_ONE_KERNEL)
+    try:
+        st, info = moe.moe_path_info(_shape(moe), 1)
+        assert st == 0 and info.startswith("one-kernel gemv path") and "layer_kernel<H=2560,I=768>" in info
+        st, info = moe.moe_path_info(_shape(moe), 512)       # the chunk path is not affected
+        assert st == 0 and info.startswith("chunk path")
+    finally:
+        moe.moe_set_decode_path(moe.PATH_THREE_KERNELS)
+    assert moe.raw().moe_set_decode_path(2) == -1
+    assert moe.raw().moe_set_decode_path(-1) == -1
+    st, info = moe.moe_path_info(_shape(moe), 1)
+    assert info.startswith("gemv path")
     st, info = moe.moe_path_info(_shape(moe, 256, 64, 16, 2), 4)
     assert st == 0 and "H=256" in info
     st, info = moe.moe_path_info(_shape(moe), 512)

@@ -31,9 +31,9 @@ def built(moe, tmp_path_factory):
 def test_compile_fills_the_cache(built):
     d, rep = built
     assert not rep["from_cache"]
-    # decode path: quant, requant, and router/gate_up/down(x2) at 4 token bounds;
-    # chunk path: router, gate_up, down(x2), combine; LM head at 4 token bounds
-    assert rep["has_chunk_path"] and rep["has_lm_head"] and rep["num_kernels"] == 2 + 16 + 5 + 4
+    # decode path: quant, requant, and router/gate_up/down(x2)/layer at 4 token
+    # bounds; chunk path: router, gate_up, down(x2), combine; LM head at 4 token bounds
+    assert rep["has_chunk_path"] and rep["has_lm_head"] and rep["num_kernels"] == 2 + 20 + 5 + 4
     path = rep["cache_file"]
     assert os.path.dirname(path) == str(d) and os.path.basename(path).startswith("moe_H1024_I384_gfx950_")
     assert os.path.getsize(path) > 10_000
