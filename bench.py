@@ -76,7 +76,9 @@ def parse():
                    help="skip the 4-token verify-window router constructions (32 and 20 distinct experts)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
-    p.add_argument("--tokens", type=str, default="1,4", help="token counts to time (the first is the reported value)")
+    p.add_argument("--tokens", type=str, default="1,4",
+                   help="token counts to time (the first is the reported value); 4 also times 4x32 and 4x20 "
+                        "(the verify-window routers) unless --no-verify; 4x32 or 4x20 alone time just that one")
     p.add_argument("--experts", type=int, default=256, help="routed experts per layer (512 is Ling-3.0-flash's own)")
     p.add_argument("--chunk-tokens", type=int, default=512, help="tokens of the chunk measurement (0: skip)")
     p.add_argument("--chunk-steps", type=int, default=400, help="timed chunk layer forwards")
@@ -129,7 +131,14 @@ def main() -> int:
     out = torch.empty((8, H), dtype=torch.float32, device="cuda")
 
     workloads = []
-    for M in [int(v) for v in args.tokens.split(",")]:
+    for tok in args.tokens.split(","):
+        if "x" in tok:                      # "4x32": 4 tokens, verify router with 32 distinct experts
+            m, d = (int(v) for v in tok.split("x"))
+            if m != 4 or d not in (20, 32):
+                raise SystemExit(f"--tokens {tok}: the verify construction is 4x32 or 4x20")
+            workloads.append((tok, m, d))
+            continue
+        M = int(tok)
         workloads.append((str(M), M, None))
         if M == 4 and args.verify:
             # the verify window as configured: biased routers giving 32
@@ -544,6 +553,7 @@ def chunk_bench(args, moe, synth, stack, shp, stream) -> dict:
                      "tflops_down_kernel": round(flops_down / (kus["down"] * 1e-6) / 1e12, 1),
                      "util_vs_fp4_peak": round(mfma_layer / FP4_PEAK_TFLOPS, 4),
                      "util_vs_fp8_peak": round(mfma_layer / FP8_PEAK_TFLOPS, 4)},
+            "mfma_counters": measured_chunk_mfma(),
             "workload": f"{M}-token chunk per layer, Zipf-1.1 routing through a bias channel, cold 40-layer walk, "
                         "hip graph"}
 
@@ -572,6 +582,33 @@ def measured_traffic():
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# Matrix-core counters of the chunk kernels (rocprofv3 --pmc), reported only
+# while the chunk kernels' sources are the ones they were taken on.
+CHUNK_MFMA_FILE = "profiles/chunk_mfma_counters_ling_zipf512.txt"
+
+
+def measured_chunk_mfma():
+    from mxfp4_weight_streaming_amd.profiling import chunk_source_hash
+    path = os.path.join(ROOT, CHUNK_MFMA_FILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "command")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("chunk_source_sha256") != chunk_source_hash():
+        return None
+    try:
+        return {"gate_up_busy_util": float(fields["gate_up_mfma_busy_util"]),
+                "down_busy_util": float(fields["down_mfma_busy_util"]),
+                "executed_over_algorithmic_ops": float(fields["gate_up_executed_over_algorithmic_ops"]),
+                "basis": "SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' active cycles; the FP8 x FP4 scaled MFMA issues "
+                         "at 32 cycles per 16x16x128 (the dense FP8 rate), and the 16-row tiles are padded"}
     except (KeyError, ValueError):
         return None
 

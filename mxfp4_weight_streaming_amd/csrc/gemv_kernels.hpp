@@ -500,34 +500,41 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
         u32x4 wg[CPL], wu[CPL];
         uint32_t sg[NSW], su[NSW];
     };
-    auto issue = [&](int item, Stage& st) {
+    // dummy: the look-ahead past a workgroup's last item.  Its loads are still
+    // issued (the waits then stay exact, see below), but every lane reads the
+    // first 16 bytes of the item's expert, so each instruction fetches one
+    // line instead of the item's rows again (those re-reads were a fifth of
+    // the gate/up traffic at four tokens: the loads are non-temporal).
+    auto issue = [&](int item, Stage& st, bool dummy = false) {
         const int slot = item / BPE, rb = item % BPE;
         const int e = rl.act_experts[slot];
         const bool shared = e == kSharedExpert;
-        const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const int r = dummy ? 0 : rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
+        const int lo = dummy ? 0 : li;                  // lane's first chunk / scale dword
+        const int step = dummy ? 0 : LPR;
         const uint8_t* w13e = shared ? a.sh.w13 : a.w13 + (size_t)e * 2 * I * (H / 2);
         const uint8_t* s13e = shared ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * CH;
         const u32x4* grow = (const u32x4*)(w13e + (size_t)r * (H / 2));
-        const u32x4* urow = grow + (size_t)I * CH;
+        const u32x4* urow = dummy ? grow : grow + (size_t)I * CH;
         const uint8_t* gsc = s13e + (size_t)r * CH;
-        const uint8_t* usc = gsc + (size_t)I * CH;
+        const uint8_t* usc = dummy ? gsc : gsc + (size_t)I * CH;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            st.wg[i] = load_stream(grow + li + LPR * i);
-            st.wu[i] = load_stream(urow + li + LPR * i);
+            st.wg[i] = load_stream(grow + lo + step * i);
+            st.wu[i] = load_stream(urow + lo + step * i);
         }
         if constexpr (kScaleDw) {
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
-                const int d = min(li + LPR * j, CH / 4 - 1);       // past the row's end: its last dword again
+                const int d = min(lo + step * j, CH / 4 - 1);      // past the row's end: its last dword again
                 st.sg[j] = reinterpret_cast<const uint32_t*>(gsc)[d];
                 st.su[j] = reinterpret_cast<const uint32_t*>(usc)[d];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                st.sg[i] = gsc[li + LPR * i];
-                st.su[i] = usc[li + LPR * i];
+                st.sg[i] = gsc[lo + step * i];
+                st.su[i] = usc[lo + step * i];
             }
         }
     };
@@ -598,8 +605,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     issue(blockIdx.x, st[0]);
     if constexpr (IPW <= 4) {
         // Unrolled over IPW items, with the look-ahead unconditional (past the
-        // last item, this item's rows again, unused; none from the IPW-th item,
-        // whose successor the loop below loads itself): the two stages are never
+        // last item, a dummy issue, unused; none from the IPW-th item, whose
+        // successor the loop below loads itself): the two stages are never
         // carried around a loop edge (register copies there would wait for
         // the loads in flight) and each wait covers exactly the item in use.
 #pragma unroll
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             const int cur = blockIdx.x + k * gridDim.x;
             if (cur >= n_items) break;
             const int nxt = cur + gridDim.x;
-            if (k + 1 < IPW) issue(nxt < n_items ? nxt : cur, st[(k + 1) & 1]);
+            if (k + 1 < IPW) issue(nxt < n_items ? nxt : cur, st[(k + 1) & 1], nxt >= n_items);
             compute(cur, st[k & 1]);
         }
         // beyond IPW items (not reached with the launch geometry): one at a time
@@ -772,22 +779,27 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     // from whatever register, which can be one a load in flight writes)
     const uint32_t woff = __umul24((uint32_t)n, (uint32_t)(I / 2)) + (uint32_t)li * 16;
     const uint32_t soff = __umul24((uint32_t)n, (uint32_t)CH) + (uint32_t)li;
-    auto load_slot = [&](int ea_any, u32x4* wv, uint32_t* sv) {
+    // dummy (the look-ahead past a wave's last slot): the same loads, all at
+    // the expert's first 16 bytes (the offsets masked to zero, arithmetic, so
+    // the loads stay on one path), one line per instruction instead of the
+    // slot's rows again
+    auto load_slot = [&](int ea_any, u32x4* wv, uint32_t* sv, bool dummy) {
         const int ea = __builtin_amdgcn_readfirstlane(ea_any);
         const bool sh = shared && ea == kSharedExpert;
         const int e = min(max(ea, 0), a.E - 1);
         const uint8_t* wb = sh ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
         const uint8_t* sb = sh ? a.sh.s2 : a.sw2 + (size_t)e * H * CH;
+        const uint32_t keep = 0u - (uint32_t)!dummy;
 #pragma unroll
         for (int h = 0; h < RP; ++h)
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                wv[h * CPL + i] = load_stream(
-                    reinterpret_cast<const u32x4*>(wb + woff + (uint32_t)(h * RPW) * (I / 2) + LPR * 16 * i));
+                wv[h * CPL + i] = load_stream(reinterpret_cast<const u32x4*>(
+                    wb + (keep & (woff + (uint32_t)(h * RPW) * (I / 2) + LPR * 16 * i))));
 #pragma unroll
         for (int h = 0; h < RP; ++h)
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[soff + (uint32_t)(h * RPW) * CH + LPR * i];
+            for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[keep & (soff + (uint32_t)(h * RPW) * CH + LPR * i)];
         __builtin_amdgcn_sched_barrier(0);   // the slot's loads go out here, not next to their uses
     };
 
@@ -810,7 +822,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     // arguments rather than by the count of active experts (one load fewer
     // before the weights go out; past that count the id is stale but in
     // range, and its slot is never used)
-    load_slot(a.cp.act_experts[min(wave, nc - 1)], wA, sA);
+    load_slot(a.cp.act_experts[min(wave, nc - 1)], wA, sA, false);
     if (tid < nc) c_exp[tid] = ce;
     if (tid <= nc) c_off[tid] = co;
     if (tid < Pe) {
@@ -924,7 +936,7 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
         }
     };
     // slots wave, wave + 8, ...: the next slot's weights load while this one
-    // is used (past the end, the current slot's rows load again, unused).
+    // is used (past the end, a dummy load of one line, unused).
     // The loop is unrolled over the most slots a wave can have, so each step
     // is straight-line code whose waits cover exactly the slot in use.
     constexpr int NS = (MT * (kMaxTopK + 1) + G::kWaves - 1) / G::kWaves;
@@ -932,12 +944,13 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     for (int k = 0; k < NS; ++k) {
         const int slot = wave + G::kWaves * k;
         if (slot >= n_act) break;
-        const int next = slot + G::kWaves < n_act ? slot + G::kWaves : slot;
+        const bool past = slot + G::kWaves >= n_act;
+        const int next = past ? slot : slot + G::kWaves;
         if (k % 2 == 0) {
-            load_slot(c_exp[next], wB, sB);
+            load_slot(c_exp[next], wB, sB, past);
             consume(slot, wA, sA);
         } else {
-            load_slot(c_exp[next], wA, sA);
+            load_slot(c_exp[next], wA, sA, past);
             consume(slot, wB, sB);
         }
     }
