@@ -35,6 +35,34 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
+// fl32(x / s) as far as its E4M3 code goes, for the activation quantisation
+// (s = fl32(amax / 448) of a token, r = fl32(1 / s), both once per token):
+// the product q0 = x * r corrected once by its residual, fma(x - q0 s, r, q0).
+// For every bf16 amax >= 2^-64 and every bf16 x with |x| <= amax the E4M3
+// code of this value equals that of the correctly rounded quotient (checked
+// on the host over all such pairs; a negative x mirrors a positive one).
+// Below that amax (fast false, one decision per token) the residual can lose
+// bits, and the division is taken.  The quotient has the sign of x (s > 0):
+// copying it keeps -0 (fma(+0, r, -0) is +0).
+struct QuantScale {
+    float s, r;
+    bool fast;
+};
+
+__device__ __forceinline__ QuantScale quant_scale(float amax)
+{
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    return QuantScale{s, 1.0f / s, !(amax > 0.0f && amax < 0x1p-64f)};
+}
+
+__device__ __forceinline__ float quant_div(float x, const QuantScale& q)
+{
+#pragma clang fp contract(off)
+    if (!q.fast) return x / q.s;
+    const float q0 = x * q.r;
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, q.s, x), q.r, q0), x);
+}
+
 // Four values -> four E4M3 codes in one dword (byte i = value i), same
 // rounding and saturation (NaN inputs are not expected here).
 __device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, float d)

@@ -41,8 +41,9 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Per-token activation quantisation (one workgroup, one token).
-// s = amax / 448 (1 for an all-zero row), q = E4M3(x / s), both divisions
-// correctly rounded binary32 divisions.
+// s = amax / 448 (1 for an all-zero row), a correctly rounded binary32
+// division, and q = E4M3(x / s) with the code of the correctly rounded
+// quotient (quant_div).
 // ---------------------------------------------------------------------------
 template <int H>
 __device__ void quantize_token(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
@@ -55,9 +56,9 @@ __device__ void quantize_token(const uint16_t* __restrict__ x, uint8_t* __restri
     __syncthreads();
     float amax = red[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
-    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-    for (int k = threadIdx.x; k < H; k += blockDim.x) q[k] = (uint8_t)e4m3_encode(bf16_bits_to_f32(x[k]) / s);
-    if (threadIdx.x == 0) *s_out = s;
+    const QuantScale qs = quant_scale(amax);
+    for (int k = threadIdx.x; k < H; k += blockDim.x) q[k] = (uint8_t)e4m3_encode(quant_div(bf16_bits_to_f32(x[k]), qs));
+    if (threadIdx.x == 0) *s_out = qs.s;
     __syncthreads();
 }
 
@@ -215,45 +216,28 @@ __device__ void publish_route(const RouteLds& r, const RouteSrc& src, int32_t* i
     if (tid == 0) *cp.n_act = r.n_act;
 }
 
-// One token routed from its logits, in the gate/up kernel.  The workgroup's
-// slots are ranks: slot s < K is the rank-s expert with pair s (token 0), and
-// slot K the shared expert with pair K.  The weights of a slot are needed
-// before the rest of the routing, so wave 0 ranks only up to slot_me, the
-// highest slot among the workgroup's items, and the loads go out as soon as
-// those experts are known;
-// workgroup 0 ranks all K and publishes the routing and the ascending-id
-// compaction that route_prologue and publish_route would give.
-__device__ void route_rank1(const RouteSrc& src, int slot_me, RouteLds& r, int32_t* ids_out, float* w_out,
-                            const Compaction& cp)
+// One token routed from its logits, in the gate/up kernel: the ranks held by
+// wave 0 of workgroup 0 (TopkRanks, all K) are published as the routing and
+// the ascending-id compaction that route_prologue and publish_route would
+// give.  Lane r < K holds the rank-r expert.
+__device__ void publish_rank1(const TopkRanks& t, const RouteSrc& src, int32_t* ids_out, float* w_out,
+                              const Compaction& cp)
 {
-    const int tid = threadIdx.x, K = src.K;
-    const int R = blockIdx.x == 0 ? K : min(slot_me + 1, K);
-    if ((tid >> 6) == 0) topk_wave(src.logits, src.E, K, r.ids, r.w, R);
-    __syncthreads();
+    const int lane = threadIdx.x & 63, K = src.K;
     const int n = K + (src.shared ? 1 : 0);
-    if (tid <= K) {
-        r.act_experts[tid] = tid < K ? r.ids[min(tid, R - 1)] : kSharedExpert;
-        r.offsets[tid] = tid;
-        r.pair_token[tid] = 0;
-        r.pair_src[tid] = tid;
-    }
-    if (tid == 0) {
-        r.n_act = n;
-        r.offsets[n] = n;
-    }
-    if (blockIdx.x != 0) return;
-    if (tid < K) {
-        const int e = r.ids[tid];
-        int s = 0;
-        for (int q = 0; q < K; ++q) s += r.ids[q] < e ? 1 : 0;   // the K experts are distinct
-        cp.act_experts[s] = e;
+    const float w = topk_weight(t, K);
+    int s = 0;                                  // ascending-id slot: the selected experts below (distinct)
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) s += (q < K && __builtin_amdgcn_readlane(t.e, q) < t.e) ? 1 : 0;
+    if (lane < K) {
+        cp.act_experts[s] = t.e;
         cp.offsets[s] = s;
         cp.pair_token[s] = 0;
-        cp.pair_src[s] = tid;
-        if (ids_out != nullptr) ids_out[tid] = e;
-        if (w_out != nullptr) w_out[tid] = r.w[tid];
+        cp.pair_src[s] = lane;
+        if (ids_out != nullptr) ids_out[lane] = t.e;
+        if (w_out != nullptr) w_out[lane] = w;
     }
-    if (tid == 0) {
+    if (lane == 0) {
         if (src.shared) {
             cp.act_experts[K] = kSharedExpert;
             cp.pair_token[K] = 0;
@@ -351,23 +335,23 @@ __global__ __launch_bounds__(router_threads(H)) void router_kernel(RouterArgs a)
         float m = 0.0f;
 #pragma unroll
         for (int r = 0; r < NR; ++r) m = fmaxf(m, red_max[t][r]);
-        return (m == 0.0f) ? 1.0f : m / 448.0f;
+        return quant_scale(m);
     };
     if (tid < M) {
         float d = 0.0f;
 #pragma unroll
         for (int r = 0; r < NR; ++r) d += red_dot[tid][r];
         a.logits[(size_t)tid * a.E + e] = d;
-        if (blockIdx.x == 0 && a.act_q != nullptr) a.act_s[tid] = token_scale(tid);
+        if (blockIdx.x == 0 && a.act_q != nullptr) a.act_s[tid] = token_scale(tid).s;
     }
     auto quantise = [&](int item, u32x4 v) {
-        const float s = token_scale(item / NCH);
+        const QuantScale qs = token_scale(item / NCH);
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t code[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
-            code[j >> 2] |= e4m3_encode(__uint_as_float(b) / s) << (8 * (j & 3));
+            code[j >> 2] |= e4m3_encode(quant_div(__uint_as_float(b), qs)) << (8 * (j & 3));
         }
         *reinterpret_cast<u32x2*>(a.act_q + (size_t)item * 8) = u32x2{code[0], code[1]};
     };
@@ -418,7 +402,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     //    same arithmetic as the router's quantisation: s = amax / 448, codes
     //    E4M3(x / s)).  One token is split over waves 1-3, two tokens take
     //    waves 2 and 3.
-    const bool from_x = a.x != nullptr;                 // M <= 2 only
+    // (compiled for one or two tokens only: the larger kernels were measured
+    // slower with this code in them, unused)
+    const bool from_x = MT <= 2 && a.x != nullptr;
     constexpr int NST = (MT * (H / 8) + 255) / 256;
     const int n8 = M * (H / 8);
     u32x2 stg[NST];
@@ -427,64 +413,71 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 #pragma unroll
         for (int j = 0; j < NST; ++j) stg[j] = ((const u32x2*)a.act_q)[min((int)threadIdx.x + 256 * j, n8 - 1)];
         s_tok = a.act_s[min((int)threadIdx.x, M - 1)];
-    } else if (wave >= M) {
-        constexpr int NC8 = H / 8, CPL8 = (NC8 + kWave - 1) / kWave;   // 16-byte chunks of a token
-        const int qw = wave - M, t = qw % M, split = (4 - M) / M, part = qw / M;
-        u32x4 xv[CPL8];
+    } else if constexpr (MT <= 2) {
+        if (wave >= M) {
+            constexpr int NC8 = H / 8, CPL8 = (NC8 + kWave - 1) / kWave;   // 16-byte chunks of a token
+            const int qw = wave - M, t = qw % M, split = (4 - M) / M, part = qw / M;
+            u32x4 xv[CPL8];
 #pragma unroll
-        for (int i = 0; i < CPL8; ++i)
-            xv[i] = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H)[min(lane + kWave * i, NC8 - 1)];
-        float m = 0.0f;
+            for (int i = 0; i < CPL8; ++i)
+                xv[i] = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H)[min(lane + kWave * i, NC8 - 1)];
+            float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPL8; ++i)
-            if (lane + kWave * i < NC8) m = fmaxf(m, amax_bf16x8(xv[i]));
-        m = wave_max(m);
-        const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
+            for (int i = 0; i < CPL8; ++i)
+                if (lane + kWave * i < NC8) m = fmaxf(m, amax_bf16x8(xv[i]));
+            const QuantScale qs = quant_scale(wave_max(m));
 #pragma unroll
-        for (int i = 0; i < CPL8; ++i) {
-            const int c = lane + kWave * i;
-            if (c < NC8 && i % split == part) {
-                const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-                uint32_t code[2] = {0u, 0u};
+            for (int i = 0; i < CPL8; ++i) {
+                const int c = lane + kWave * i;
+                if (c < NC8 && i % split == part) {
+                    const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                    uint32_t code[2] = {0u, 0u};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
-                    code[j >> 2] |= e4m3_encode(__uint_as_float(b) / s) << (8 * (j & 3));
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t b = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
+                        code[j >> 2] |= e4m3_encode(quant_div(__uint_as_float(b), qs)) << (8 * (j & 3));
+                    }
+                    act[(t * 4 + (c & 3)) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
                 }
-                act[(t * 4 + (c & 3)) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
             }
+            if (part == 0 && lane == 0) act_sl[t] = qs.s;
         }
-        if (part == 0 && lane == 0) act_sl[t] = s;
     }
-    // 1. routing, derived independently by every workgroup (the staging loads
-    //    above are in flight meanwhile); workgroup 0 publishes it for the down
-    //    kernel (and the caller).  One token routed from its logits: slots are
-    //    ranks, and a workgroup ranks only up to its own slot (route_rank1).
-    if (MT == 1 && a.src.logits != nullptr) {
-        // the workgroup's items are blockIdx.x, + gridDim.x, ...: it ranks up
-        // to the slot of its last one (the item count, (K + shared) * BPE, is
-        // known before the routing: one token's K experts are distinct)
-        const int n1 = (a.src.K + a.src.shared) * BPE;
-        int last = blockIdx.x;
-        if (last < n1) last += ((n1 - 1 - last) / (int)gridDim.x) * (int)gridDim.x;
-        route_rank1(a.src, min(last / BPE, a.src.K), rl, a.ids_out, a.w_out, a.cp);
+
+    // 1. routing.  One token routed from its logits (ranks): slots are ranks
+    //    (slot s < K is the rank-s expert with pair s, slot K the shared
+    //    expert with pair K), and wave 0 ranks the logits only up to the slot
+    //    of the workgroup's last item (the items are blockIdx.x, + gridDim.x,
+    //    ...; their count, (K + shared) * BPE, is known before the routing:
+    //    one token's K experts are distinct).  Its ranks reach the other waves
+    //    through LDS at the one barrier before the first weight loads.
+    //    Workgroup 0 ranks all K and publishes the routing for the down kernel
+    //    (and the caller).  Otherwise (caller ids, or 2+ tokens) every
+    //    workgroup derives the routing and compaction in LDS (route_prologue,
+    //    with its own barriers), and workgroup 0 publishes them.
+    const bool ranks = MT == 1 && a.src.logits != nullptr;
+    int n_items;
+    if (ranks) {
+        const int K = a.src.K;
+        n_items = (K + a.src.shared) * BPE;
+        if (wave == 0) {
+            int last = blockIdx.x;
+            if (last < n_items) last += ((n_items - 1 - last) / (int)gridDim.x) * (int)gridDim.x;
+            const int R = blockIdx.x == 0 ? K : min(last / BPE + 1, K);
+            const TopkRanks tr = topk_wave_ranks(a.src.logits, a.src.E, R);
+            if (lane < R) rl.ids[lane] = tr.e;
+            if (blockIdx.x == 0) publish_rank1(tr, a.src, a.ids_out, a.w_out, a.cp);
+        }
     } else {
         route_prologue(a.src, rl);
         if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
+        n_items = rl.n_act * BPE;
     }
-    if (!from_x) {
-#pragma unroll
-        for (int j = 0; j < NST; ++j) {
-            const int idx = threadIdx.x + 256 * j;
-            if (idx < n8) {
-                const int t = idx / (H / 8), g8 = idx % (H / 8);
-                act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
-            }
-        }
-        if ((int)threadIdx.x < M) act_sl[threadIdx.x] = s_tok;
-    }
-    __syncthreads();
-    const int n_items = rl.n_act * BPE;
+    // the expert of a slot
+    auto slot_expert = [&](int slot) -> int {
+        if (ranks) return slot < a.src.K ? rl.ids[slot] : kSharedExpert;
+        return rl.act_experts[slot];
+    };
 
     // 2. work items (selected expert, block of rows), strided over the grid;
     //    the next item's weight loads are in flight while this one computes.
@@ -507,7 +500,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     // the gate/up traffic at four tokens: the loads are non-temporal).
     auto issue = [&](int item, Stage& st, bool dummy = false) {
         const int slot = item / BPE, rb = item % BPE;
-        const int e = rl.act_experts[slot];
+        const int e = slot_expert(slot);
         const bool shared = e == kSharedExpert;
         const int r = dummy ? 0 : rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
         const int lo = dummy ? 0 : li;                  // lane's first chunk / scale dword
@@ -551,8 +544,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     auto compute = [&](int item, Stage& st) {
         const int slot = item / BPE, rb = item % BPE;
         const int r = rb * G::kRowsPerBlock + wave * G::kRowsPerWave + grp;
-        const int p0 = rl.offsets[slot];
-        const int nt = min(rl.offsets[slot + 1] - p0, MT);   // an expert has at most M <= MT tokens
+        const int p0 = ranks ? slot : rl.offsets[slot];
+        const int nt = ranks ? 1 : min(rl.offsets[slot + 1] - p0, MT);   // an expert has at most M <= MT tokens
         float accg[MT], accu[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) accg[t] = accu[t] = 0.0f;
@@ -577,7 +570,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 if (t < nt) {
-                    const int tok = rl.pair_token[p0 + t];
+                    const int tok = ranks ? 0 : rl.pair_token[p0 + t];
                     const u32x4 a0 = act[(tok * 4 + 0) * CH + c], a1 = act[(tok * 4 + 1) * CH + c];
                     const u32x4 a2 = act[(tok * 4 + 2) * CH + c], a3 = act[(tok * 4 + 3) * CH + c];
                     accg[t] += ldexp_e8m0(block_dot(hg, a0, a1, a2, a3), scg[i]);
@@ -590,9 +583,10 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             if (t < nt) {
                 accg[t] = group_sum<LPR>(accg[t]);
                 accu[t] = group_sum<LPR>(accu[t]);
-                const float sc = act_sl[rl.pair_token[p0 + t]];
+                const float sc = act_sl[ranks ? 0 : rl.pair_token[p0 + t]];
                 const float g = accg[t] * sc, u = accu[t] * sc;
-                if (li == 0) a.h[(size_t)rl.pair_src[p0 + t] * I + r] = g / (1.0f + expf(-g)) * u;
+                const int src = ranks ? slot : rl.pair_src[p0 + t];
+                if (li == 0) a.h[(size_t)src * I + r] = g / (1.0f + expf(-g)) * u;
             }
         }
     };
@@ -600,9 +594,33 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
     // Items blockIdx.x, blockIdx.x + grid, ...: the next item's loads are
     // issued before the current one is computed.
     constexpr int IPW = ((MT * kMaxTopK + 1) * BPE + 511) / 512;   // most items per workgroup
-    if ((int)blockIdx.x >= n_items) return;
+    // FP8 activations to LDS first (their loads, issued before the routing's,
+    // are in: waiting for them after the first item's loads would wait for
+    // those too, the load counter being in order).  Then, with ranks, the
+    // barrier that hands wave 0's ranks to the other waves and the first
+    // item's loads; otherwise (the routing already in LDS) the first item's
+    // loads and the barrier that makes the activations visible.
+    if (!from_x) {
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+            const int idx = threadIdx.x + 256 * j;
+            if (idx < n8) {
+                const int t = idx / (H / 8), g8 = idx % (H / 8);
+                act[(t * 4 + (g8 & 3)) * CH + (g8 >> 2)] = e4m3x8_to_half8(stg[j]);
+            }
+        }
+        if ((int)threadIdx.x < M) act_sl[threadIdx.x] = s_tok;
+    }
+    const bool has_item = (int)blockIdx.x < n_items;
     Stage st[2];
-    issue(blockIdx.x, st[0]);
+    if (ranks) {
+        __syncthreads();
+        if (has_item) issue(blockIdx.x, st[0]);
+    } else {
+        if (has_item) issue(blockIdx.x, st[0]);
+        __syncthreads();
+    }
+    if (!has_item) return;
     if constexpr (IPW <= 4) {
         // Unrolled over IPW items, with the look-ahead unconditional (past the
         // last item, a dummy issue, unused; none from the IPW-th item, whose

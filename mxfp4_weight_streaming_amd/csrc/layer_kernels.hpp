@@ -235,24 +235,23 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a)
             }
             if (first) {
                 // every token's FP8 codes as f16 in LDS: s = amax / 448, codes
-                // E4M3(x / s), both correctly rounded divisions (the router
-                // kernel's quantisation)
+                // E4M3(x / s) (the router kernel's quantisation)
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     if (t < M && own) {
                         float m = 0.0f;
 #pragma unroll
                         for (int r = 0; r < NR; ++r) m = fmaxf(m, red_max[t][r]);
-                        const float s = (m == 0.0f) ? 1.0f : m / 448.0f;
+                        const QuantScale qs = quant_scale(m);
                         const uint32_t vv[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
                         uint32_t code[2] = {0u, 0u};
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const uint32_t bb = (j & 1) ? (vv[j >> 1] & 0xFFFF0000u) : (vv[j >> 1] << 16);
-                            code[j >> 2] |= e4m3_encode(__uint_as_float(bb) / s) << (8 * (j & 3));
+                            code[j >> 2] |= e4m3_encode(quant_div(__uint_as_float(bb), qs)) << (8 * (j & 3));
                         }
                         act[(t * 4 + (c & 3)) * CH + (c >> 2)] = e4m3x8_to_half8(u32x2{code[0], code[1]});
-                        if (c == 0) act_sl[t] = s;
+                        if (c == 0) act_sl[t] = qs.s;
                     }
                 }
             }

@@ -382,7 +382,9 @@ moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hid
     // One or two tokens: the gate/up kernel quantises the activations itself
     // (its waves that derive no routing do it during the routing prologue),
     // so the router only computes logits.  More tokens: the router quantises
-    // them, a slice per workgroup.
+    // them, a slice per workgroup.  (The router quantising one token too
+    // makes gate_up 0.4 us shorter but the graph-replayed layer 0.3 us
+    // longer, measured.)
     const bool one = M <= 2;
     if ((st = enqueue_router(shape, M, hidden, router_w, one ? nullptr : q, one ? nullptr : sc, c, s, ev(0))) !=
         MOE_OK)

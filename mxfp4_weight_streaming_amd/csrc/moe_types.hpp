@@ -79,8 +79,9 @@ struct GateUpArgs {
     const float* act_s;    // [M]
     float* h;              // [M*K (+M),I]
     SharedWeights sh;      // read when the compaction holds the shared slot
-    const uint16_t* x;     // [M,H] bf16, or nullptr.  When set (M <= 2), the
-                           // kernel quantises x itself and act_q/act_s are unused
+    const uint16_t* x;     // [M,H] bf16, or nullptr.  When set (M <= 2; ignored
+                           // by the kernels for more tokens), the kernel
+                           // quantises x itself and act_q/act_s are unused
 };
 
 struct DownArgs {

@@ -48,13 +48,19 @@ __device__ __forceinline__ void lane_sort_step(uint32_t* u, int* s, int a, int b
     s[b] = sw ? sa : sb;
 }
 
-// The selection on keys already held by the lanes: lane l holds the keys of
+// The ranks of the selection, in registers: lane r < R ends with the rank-r
+// expert (e) and its key (u); top is the largest key (in every lane).
+struct TopkRanks {
+    int e;
+    uint32_t u;
+    uint32_t top;
+};
+
+// The R rounds on keys already held by the lanes: lane l holds the keys of
 // experts l + 64 i in u[i] (0 for experts past E), s[i] = i.  Sorts each
-// lane's entries, then runs the R rounds; writes ids_out[0..R) and, when
-// R == K, the softmax weights w_out[0..K).
+// lane's entries first.
 template <int PER>
-__device__ __forceinline__ void topk_select_t(uint32_t (&u)[PER], int (&s)[PER], int K, int32_t* ids_out,
-                                              float* w_out, int R)
+__device__ __forceinline__ TopkRanks topk_rounds_t(uint32_t (&u)[PER], int (&s)[PER], int R)
 {
     const int lane = threadIdx.x & 63;
     // sorting network over the lane's entries (a strict order: slots differ)
@@ -99,16 +105,34 @@ __device__ __forceinline__ void topk_select_t(uint32_t (&u)[PER], int (&s)[PER],
             s[PER - 1] = PER;
         }
     }
+    return TopkRanks{my_e, my_u, top};
+}
+
+// The softmax weight of lane r's selection (r < K; 0 in the other lanes).
+__device__ __forceinline__ float topk_weight(const TopkRanks& t, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const float lmax = f32_from_orderable(t.top);
+    const float ex = (lane < K) ? expf(f32_from_orderable(t.u) - lmax) : 0.0f;
+    return ex / wave_sum(ex);
+}
+
+// The selection: the R rounds, then ids_out[0..R) and, when R == K, the
+// softmax weights w_out[0..K).
+template <int PER>
+__device__ __forceinline__ void topk_select_t(uint32_t (&u)[PER], int (&s)[PER], int K, int32_t* ids_out,
+                                              float* w_out, int R)
+{
+    const int lane = threadIdx.x & 63;
+    const TopkRanks t = topk_rounds_t<PER>(u, s, R);
     if (R < K) {                                // the first R ranks only: their experts
-        if (lane < R) ids_out[lane] = my_e;
+        if (lane < R) ids_out[lane] = t.e;
         return;
     }
-    const float lmax = f32_from_orderable(top);
-    const float ex = (lane < K) ? expf(f32_from_orderable(my_u) - lmax) : 0.0f;
-    const float den = wave_sum(ex);
+    const float w = topk_weight(t, K);
     if (lane < K) {
-        ids_out[lane] = my_e;
-        w_out[lane] = ex / den;
+        ids_out[lane] = t.e;
+        w_out[lane] = w;
     }
 }
 
@@ -142,6 +166,33 @@ __device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t*
         s[i] = i;
     }
     topk_select_t<PER>(u, s, K, ids_out, w_out, R);
+}
+
+// The first R ranks of one token's E logits by one wave, in registers (see
+// TopkRanks).  Inlined: its callers keep the result in registers.
+template <int PER>
+__device__ __forceinline__ TopkRanks topk_ranks_t(const float* Lg, int E, int R)
+{
+    const int lane = threadIdx.x & 63;
+    const __attribute__((address_space(1))) float* L = (const __attribute__((address_space(1))) float*)Lg;
+    uint32_t u[PER];
+    int s[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + kWave * i;
+        u[i] = topk_key(L[e < E ? e : E - 1], e < E);
+        s[i] = i;
+    }
+    return topk_rounds_t<PER>(u, s, R);
+}
+
+// topk_ranks_t with the logits-per-lane count chosen by E (wave-uniform).
+__device__ __forceinline__ TopkRanks topk_wave_ranks(const float* L, int E, int R)
+{
+    if (E <= 64) return topk_ranks_t<1>(L, E, R);
+    if (E <= 128) return topk_ranks_t<2>(L, E, R);
+    if (E <= 256) return topk_ranks_t<4>(L, E, R);
+    return topk_ranks_t<8>(L, E, R);
 }
 
 // Top-K of one token's E logits by one wave: ids_out[r] is the rank-r expert
