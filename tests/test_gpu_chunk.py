@@ -4,10 +4,16 @@ scaled FP4xFP8 matrix cores) against the CPU oracle, through the C ABI.
 The criteria are the decode path's (P1-P5).  At the tiny shape
 (H=256, I=64, E=16, K=2) whole layers are compared for every token.  At the
 Ling shape the routing of all tokens is compared; the expert stages are
-compared on sampled tokens, because an expert layer's output for a token
-depends only on that token, and the oracle takes ~0.15 s per (token, expert)
-pair there.
+compared on chosen tokens, because an expert layer's output for a token
+depends only on that token, and the oracle takes ~0.1 s per (token, expert)
+pair there (its calls run on a pool of threads: the C oracle releases the
+interpreter lock).  The chosen tokens at the 512-token Zipf chunk: every
+token of the most-selected expert (all rows of all its chunk records), and
+one token in a chunk record of each size (4, 3, 2 and 1 tiles of 16 rows).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -279,6 +285,38 @@ def _sample_tokens(ids, r, n_hot=3):
     return sorted({t for t in pick if ok[t]})
 
 
+def _pool_map(fn, items):
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        return list(ex.map(fn, items))
+
+
+def _record_class_pairs(ids):
+    """(token, j) of one pair per chunk-record size.  An expert's n pairs (in
+    ascending token order) form n // 64 records of four 16-row tiles, then
+    one record of ceil((n % 64) / 16) tiles; the pair taken is the last row of
+    the expert's last record (for four tiles: of its first record)."""
+    cnt = np.bincount(ids.ravel(), minlength=256)
+    out = {}
+    for e in np.nonzero(cnt)[0]:
+        n, rem = int(cnt[e]), int(cnt[e]) % 64
+        tiles = 4 if rem == 0 else (rem + 15) // 16
+        pos = 63 if tiles == 4 else n - 1
+        if tiles in out or (tiles == 4 and n < 64):
+            continue
+        t, j = np.nonzero(ids == e)
+        out[tiles] = (int(t[pos]), int(j[pos]))
+    assert set(out) == {1, 2, 3, 4}, out
+    return [out[k] for k in sorted(out)]
+
+
+def _chosen_pairs(ids):
+    """Every (token, j) of the most-selected expert, then the record-class pairs."""
+    hot = int(np.argmax(np.bincount(ids.ravel(), minlength=256)))
+    t, j = np.nonzero(ids == hot)
+    pairs = list(zip(t.tolist(), j.tolist()))
+    return pairs + [p for p in _record_class_pairs(ids) if p not in pairs], hot
+
+
 def test_chunk_route_ling_zipf_512(moe, ling, zipf512):
     li, dw, r = zipf512
     shp = _shape(moe, li)
@@ -324,6 +362,68 @@ def test_chunk_layer_ling_zipf_512_sampled(moe, ling, zipf512):
     t = oracle.moe_layer(li.x[toks], li.wts.wr, li.wts.w13, li.wts.s13, li.wts.w2, li.wts.s2, li.K)
     err = rel_l2(got[toks], t.out)
     assert err <= 1e-2, err
+
+
+def test_chunk_gate_up_ling_zipf_512_hot_expert(moe, ling, zipf512):
+    """P3 for every pair of the most-selected expert (~330 tokens: several
+    4-tile records and a partial one, every tile row) and one pair per
+    chunk-record size."""
+    li, dw, r = zipf512
+    shp = _shape(moe, li)
+    q, s = oracle.quant_act(li.x)
+    h, q2, s2 = _gate_up(moe, shp, li.M, q, s, r.ids, dw, moe.workspace(shp, li.M))
+    pairs, hot = _chosen_pairs(r.ids)
+    assert len(pairs) > 200, len(pairs)
+    groups = [pairs[i:i + 8] for i in range(0, len(pairs), 8)]
+
+    def ref(g):
+        ts = [t for t, _ in g]
+        e = np.array([[r.ids[t, j]] for t, j in g], np.int32)
+        return oracle.gate_up(q[ts], s[ts], e, li.wts.w13, li.wts.s13, shp.inter)
+    h_ref = np.concatenate(_pool_map(ref, groups))
+    rows = np.array([t * li.K + j for t, j in pairs])
+    err = _check_gate_up_rows(h[rows], q2[rows], s2[rows], h_ref)
+    print(f"hot expert {hot}: {len(pairs)} pairs, h rel_l2 {err:.2e}", flush=True)
+
+
+def test_chunk_down_ling_zipf_512_hot_expert_tokens(moe, ling, zipf512):
+    """Down + combine (seeded FP8 intermediates) for every token of the
+    most-selected expert and the record-class tokens, all K pairs each."""
+    li, dw, r = zipf512
+    shp = _shape(moe, li)
+    rng = np.random.default_rng(78)
+    P, I = li.M * li.K, shp.inter
+    q2 = rng.integers(0, 256, (P, I), dtype=np.uint8)
+    q2[(q2 & 0x7F) == 0x7F] = 0x00                     # no NaN codes
+    s2 = (2.0 ** rng.uniform(-8, -2, P)).astype(np.float32)
+    got = _down(moe, shp, li.M, q2, s2, r.ids, r.w, dw, moe.workspace(shp, li.M))
+    toks = sorted({t for t, _ in _chosen_pairs(r.ids)[0]})
+    groups = [toks[i:i + 4] for i in range(0, len(toks), 4)]
+
+    def ref(g):
+        rows = np.array([t * li.K + j for t in g for j in range(li.K)])
+        return oracle.down_combine(q2[rows], s2[rows], r.ids[g], r.w[g], li.wts.w2, li.wts.s2, shp.hidden)
+    out_ref = np.concatenate(_pool_map(ref, groups))
+    errs = [rel_l2(got[t:t + 1], out_ref[i:i + 1]) for i, t in enumerate(toks)]
+    assert max(errs) <= 1e-3, (max(errs), toks[int(np.argmax(errs))])
+
+
+def test_chunk_layer_ling_zipf_512_hot_expert_tokens(moe, ling, zipf512):
+    """P5, token by token, for every token of the most-selected expert and the
+    record-class tokens (unflagged ones: the GPU routes them as the oracle)."""
+    li, dw, r = zipf512
+    shp = _shape(moe, li)
+    got = _forward(moe, shp, li, dw, moe.workspace(shp, li.M))
+    toks = sorted({t for t, _ in _chosen_pairs(r.ids)[0] if r.gap[t] >= 1e-4})
+    assert len(toks) > 200, len(toks)
+    groups = [toks[i:i + 2] for i in range(0, len(toks), 2)]
+
+    def ref(g):
+        return oracle.moe_layer(li.x[g], li.wts.wr, li.wts.w13, li.wts.s13, li.wts.w2, li.wts.s2, li.K).out
+    out_ref = np.concatenate(_pool_map(ref, groups))
+    errs = [rel_l2(got[t:t + 1], out_ref[i:i + 1]) for i, t in enumerate(toks)]
+    print(f"{len(toks)} tokens: worst rel_l2 {max(errs):.2e}", flush=True)
+    assert max(errs) <= 1e-2, (max(errs), toks[int(np.argmax(errs))])
 
 
 def test_chunk_layer_ling_ragged_40_sampled(moe, ling):
