@@ -324,28 +324,33 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
             a.pos_of[p] = pos;
         }
     }
-    // chunk list, from the expert's own thread (its count cc and slot_e): its
-    // 4-tile chunks first, then its last chunk in the group of its tile count;
-    // two scans, each packing two counters
-    const int rem = cc % kChunkRows;
-    const int full = cc / kChunkRows + (rem > 3 * 16 ? 1 : 0);
-    const int last_tiles = (rem > 0 && rem <= 3 * 16) ? (rem + 15) / 16 : 0;
-    int t43 = 0, t21 = 0;
-    const int s43 = block_excl_scan((full << 16) | (last_tiles == 3 ? 1 : 0), tmp, t43);
-    const int s21 = block_excl_scan(((last_tiles == 2 ? 1 : 0) << 16) | (last_tiles == 1 ? 1 : 0), tmp, t21);
-    const int at4 = s43 >> 16, at3 = s43 & 0xFFFF, at2 = s21 >> 16, at1 = s21 & 0xFFFF;
-    const int n4 = t43 >> 16, n3 = t43 & 0xFFFF, n2 = t21 >> 16, n1 = t21 & 0xFFFF;
-    if (cc > 0) {
-        for (int k = 0; k < full; ++k) {
-            const int rows = cc - k * kChunkRows;
-            a.chunks.rec[at4 + k] = make_int4(rec_e, off_e + k * kChunkRows, rows < kChunkRows ? rows : kChunkRows, 0);
+    // chunk list, from the expert's own thread (its count cc and slot_e): a
+    // busy expert's (more than kChunkRows rows) chunks first, cut evenly into
+    // at most kBigChunkRows rows each; then the others in the group of their
+    // tile count, 4 tiles down to 1; two scans, packing the group counters
+    // (the big chunks in 16 bits, the tile groups in 10-bit fields: at most
+    // kMaxExperts + 1 experts each)
+    const bool big = cc > kChunkRows;
+    const int nbig = big ? (cc + kBigChunkRows - 1) / kBigChunkRows : 0;
+    const int tiles = (!big && cc > 0) ? (cc + 15) / 16 : 0;
+    int tb4 = 0, t321 = 0;
+    const int sb4 = block_excl_scan((nbig << 16) | (tiles == 4 ? 1 : 0), tmp, tb4);
+    const int s321 = block_excl_scan(((tiles == 3 ? 1 : 0) << 20) | ((tiles == 2 ? 1 : 0) << 10) | (tiles == 1 ? 1 : 0),
+                                     tmp, t321);
+    const int atb = sb4 >> 16, at4 = sb4 & 0xFFFF;
+    const int at3 = s321 >> 20, at2 = (s321 >> 10) & 0x3FF, at1 = s321 & 0x3FF;
+    const int nb = tb4 >> 16, n4 = tb4 & 0xFFFF, n3 = t321 >> 20, n2 = (t321 >> 10) & 0x3FF, n1 = t321 & 0x3FF;
+    if (big) {
+        const int q = (cc + nbig - 1) / nbig;           // rows per chunk; the last takes the rest
+        for (int k = 0; k < nbig; ++k) {
+            const int rows = cc - k * q;
+            a.chunks.rec[atb + k] = make_int4(rec_e, off_e + k * q, rows < q ? rows : q, 0);
         }
-        if (last_tiles > 0) {
-            const int idx = n4 + (last_tiles == 3 ? at3 : last_tiles == 2 ? n3 + at2 : n3 + n2 + at1);
-            a.chunks.rec[idx] = make_int4(rec_e, off_e + full * kChunkRows, rem, 0);
-        }
+    } else if (tiles > 0) {
+        const int idx = nb + (tiles == 4 ? at4 : tiles == 3 ? n4 + at3 : tiles == 2 ? n4 + n3 + at2 : n4 + n3 + n2 + at1);
+        a.chunks.rec[idx] = make_int4(rec_e, off_e, cc, 0);
     }
-    const int n_chunks = n4 + n3 + n2 + n1;
+    const int n_chunks = nb + n4 + n3 + n2 + n1;
     for (int i = n_chunks + tid; i < a.chunks.C; i += kSortThreads) a.chunks.rec[i] = make_int4(0, 0, 0, 0);
     if (tid == 0) *a.chunks.n_chunks = n_chunks;
 }
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
 // ---------------------------------------------------------------------------
 // Gate/up: workgroup (chunk, jq) owns the kGuRows = 16 NJ intermediate rows
 // j = kGuRows jq .. +kGuRows-1 of the chunk's expert, for both the gate (rows j)
-// and the up (rows I + j) projection, over the chunk's (at most 64) tokens.
+// and the up (rows I + j) projection, over the chunk's tokens (at most
+// kBigChunkRows).
 // Its waves split K = H into KSPLIT slices: each wave issues all the weight
 // loads of its slice at once (NJ n-tiles of gate and of up, so one activation
 // operand feeds 2 NJ MFMAs), together with the token ids of every tile of the
@@ -416,12 +422,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             raw[t][i] = load_stream(reinterpret_cast<const u32x4*>(nt + (size_t)(b / BPR) * (H / 2) + (b % BPR) * 16));
         }
     }
-    int tok[kChunkTiles];
-#pragma unroll
-    for (int tt = 0; tt < kChunkTiles; ++tt) {
+    // token of this lane's row in tile tt (past the chunk: its last row again)
+    auto tok_of = [&](int tt) {
         const int row = tt * 16 + r;
-        tok[tt] = a.cp.pair_token[off + (row < n ? row : n - 1)];
-    }
+        return a.cp.pair_token[off + (row < n ? row : n - 1)];
+    };
+    const int tok0 = tok_of(0);
+    int tok_next = tok_of(1);
     const uint8_t* s13e = e == kSharedExpert ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * SROW;
     copy_to_lds(sc_lds[0], s13e + (size_t)j0 * SROW, kGuRows * SROW);
     copy_to_lds(sc_lds[1], s13e + (size_t)(I + j0) * SROW, kGuRows * SROW);
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
         s_row = a.act_s[t];
     };
-    load_tile(tok[0]);
+    load_tile(tok0);
     // into the operand layout through the wave's LDS area: lane (r, g) of
     // k-step q takes block 4 q + g of row r (the row stride of BPR + 1 blocks
     // keeps the 16 rows of one read on distinct banks)
@@ -473,9 +480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
     }
     const int ntiles = (n + 15) / 16;
-#pragma unroll
-    for (int tile = 0; tile < kChunkTiles; ++tile) {
-        if (tile >= ntiles) break;
+    for (int tile = 0; tile < ntiles; ++tile) {
         f32x4 accg[NJ], accu[NJ];
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
@@ -500,7 +505,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             }
         }
         if (w == 0 && g == 0) tok_scale[r] = s_row;
-        if (tile + 1 < ntiles) load_tile(tok[tile + 1 < kChunkTiles ? tile + 1 : 0]);   // in flight meanwhile
+        // the token ids two tiles ahead, then the next tile's activations (its
+        // ids loaded a tile ago), all in flight while this tile is reduced
+        const int tok_after = tok_of(tile + 2);
+        if (tile + 1 < ntiles) load_tile(tok_next);
+        tok_next = tok_after;
         __syncthreads();
         // thread (ii, l) finalises C[4 (l >> 4) + ii][l & 15] of each n-tile
         const int l = threadIdx.x & 63, ii = threadIdx.x >> 6;

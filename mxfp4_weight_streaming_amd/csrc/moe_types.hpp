@@ -124,8 +124,12 @@ struct ChunkTopkArgs {
 };
 
 // Work list of the grouped kernels: the sorted rows of each active expert
-// cut into chunks of at most kChunkRows rows, larger chunks first.
+// as chunks, larger chunks first.  An expert with at most kChunkRows rows is
+// one chunk (1-4 tiles of 16 rows); a busier one is cut evenly into chunks of
+// at most kBigChunkRows rows, so that a workgroup reads its rows' weights
+// once for up to 16 tiles of tokens instead of once per 64 tokens.
 constexpr int kChunkRows = 64;
+constexpr int kBigChunkRows = 256;
 
 struct ChunkList {
     int32_t* n_chunks;     // [1]
@@ -133,6 +137,8 @@ struct ChunkList {
     int C;                 // entries of rec (chunk_bound)
 };
 
+// chunks of S active experts over P rows: at most one per expert plus one
+// per kChunkRows rows of the busy ones
 __host__ __device__ constexpr int chunk_bound(int S, int P) { return S + (P + kChunkRows - 1) / kChunkRows; }
 
 struct SortArgs {
@@ -333,10 +339,10 @@ __host__ __device__ constexpr bool layer_shape_ok(int H, int I)
            layer_down_blocks(I) * layer_down_passes(H, I) <= 6 && H % (layer_down_rows_per_pass(I) * layer_down_passes(H, I)) == 0;
 }
 
-// Chunk path blocking: 16-row MFMA tiles, 64-row chunks, 32 gate/up rows and
+// Chunk path blocking: 16-row MFMA tiles, chunks of up to 64 rows (256 for a
+// busy expert), 32 gate/up rows and
 // 256 down rows per workgroup (4 waves x kDnNJ = 4 n-tiles of 16 rows), router
 // K slices of H/8.  The chunk path therefore needs H % 256 == 0.
-constexpr int kChunkTiles = kChunkRows / 16;
 constexpr int kGuNJ = 2;                                // 16-row n-tiles per wave and matrix
 constexpr int kGuRows = 16 * kGuNJ;
 constexpr int kDnNJ = 4;

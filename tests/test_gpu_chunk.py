@@ -8,8 +8,9 @@ compared on chosen tokens, because an expert layer's output for a token
 depends only on that token, and the oracle takes ~0.1 s per (token, expert)
 pair there (its calls run on a pool of threads: the C oracle releases the
 interpreter lock).  The chosen tokens at the 512-token Zipf chunk: every
-token of the most-selected expert (all rows of all its chunk records), and
-one token in a chunk record of each size (4, 3, 2 and 1 tiles of 16 rows).
+token of the most-selected expert (all rows of both its 166-row chunk
+records), and one token in a chunk record of each kind (4, 3, 2 and 1 tiles
+of 16 rows, and a busy expert's record of more than 64 rows).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -291,22 +292,21 @@ def _pool_map(fn, items):
 
 
 def _record_class_pairs(ids):
-    """(token, j) of one pair per chunk-record size.  An expert's n pairs (in
-    ascending token order) form n // 64 records of four 16-row tiles, then
-    one record of ceil((n % 64) / 16) tiles; the pair taken is the last row of
-    the expert's last record (for four tiles: of its first record)."""
+    """(token, j) of one pair per chunk-record kind.  An expert's n pairs (in
+    ascending token order) are one record of ceil(n / 16) tiles when n <= 64
+    (kinds 1-4), else records of up to 256 rows cut evenly (kind 'big'); the
+    pair taken is the expert's last row."""
     cnt = np.bincount(ids.ravel(), minlength=256)
     out = {}
     for e in np.nonzero(cnt)[0]:
-        n, rem = int(cnt[e]), int(cnt[e]) % 64
-        tiles = 4 if rem == 0 else (rem + 15) // 16
-        pos = 63 if tiles == 4 else n - 1
-        if tiles in out or (tiles == 4 and n < 64):
+        n = int(cnt[e])
+        kind = "big" if n > 64 else (n + 15) // 16
+        if kind in out:
             continue
         t, j = np.nonzero(ids == e)
-        out[tiles] = (int(t[pos]), int(j[pos]))
-    assert set(out) == {1, 2, 3, 4}, out
-    return [out[k] for k in sorted(out)]
+        out[kind] = (int(t[-1]), int(j[-1]))
+    assert set(out) == {1, 2, 3, 4, "big"}, out
+    return [out[k] for k in (4, 3, 2, 1, "big")]
 
 
 def _chosen_pairs(ids):
@@ -365,9 +365,8 @@ def test_chunk_layer_ling_zipf_512_sampled(moe, ling, zipf512):
 
 
 def test_chunk_gate_up_ling_zipf_512_hot_expert(moe, ling, zipf512):
-    """P3 for every pair of the most-selected expert (~330 tokens: several
-    4-tile records and a partial one, every tile row) and one pair per
-    chunk-record size."""
+    """P3 for every pair of the most-selected expert (~330 tokens: two records
+    of 11 tiles, every tile row) and one pair per chunk-record kind."""
     li, dw, r = zipf512
     shp = _shape(moe, li)
     q, s = oracle.quant_act(li.x)
