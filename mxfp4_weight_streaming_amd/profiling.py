@@ -257,14 +257,15 @@ def sweep(out_path: str, runs) -> None:
     lines += ["timing: HIP events around the graph replays; GB/s = algorithmic bytes (selected experts' MXFP4 codes "
               "+ scales, bf16 router, x, out) / time; kernel columns: start/stop events stamped by each launch", "",
               f"{'experts':>7s} {'tokens':>6s} {'distinct':>8s} {'us/layer':>9s} {'GB/s':>7s} {'%8TB/s':>7s} "
-              f"{'router':>7s} {'gate_up':>8s} {'down':>7s}"]
+              f"{'router':>7s} {'gate_up':>8s} {'down':>7s}",
+              "(tokens 4x32 / 4x20: the 4-token verify routers with 32 / 20 distinct experts)"]
     chunks = []
     for _, path in runs:
         d = json.loads(open(path).read().strip().splitlines()[-1])
         E = d["config"]["experts"]
-        for M, r in sorted(d["by_tokens"].items(), key=lambda kv: int(kv[0])):
+        for M, r in sorted(d["by_tokens"].items(), key=lambda kv: (int(kv[0].split("x")[0]), kv[0])):
             k = r["kernel_us"]
-            lines.append(f"{E:7d} {int(M):6d} {r['mean_distinct_experts']:8.2f} {r['us_per_layer']:9.2f} {r['gbs']:7.0f} "
+            lines.append(f"{E:7d} {M:>6s} {r['distinct_experts']:8.2f} {r['us_per_layer']:9.2f} {r['gbs']:7.0f} "
                          f"{r['pct_of_hbm_peak']:7.2f} {k['router']:7.2f} {k['gate_up']:8.2f} {k['down']:7.2f}")
         if d.get("chunk"):
             c = d["chunk"]
