@@ -217,7 +217,10 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t pre[kMaxExperts];
     __shared__ int32_t tmp[kSortThreads / kWave];
-    const int P = a.M * a.K, K = a.K, E = a.E, W = (a.M + 31) >> 5;
+    // W mask words per expert, stored WS = W | 1 words apart: an odd stride
+    // puts the same word of different experts' masks (read together by the
+    // threads of a wave) on different LDS banks
+    const int P = a.M * a.K, K = a.K, E = a.E, W = (a.M + 31) >> 5, WS = W | 1;
     const int tid = threadIdx.x;
     auto clamp_e = [&](int e) { return e < 0 ? 0 : (e >= E ? E - 1 : e); };
     // every pair's expert, loaded once (all loads first)
@@ -227,14 +230,14 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
         const int p = tid + kSortThreads * i;
         eid[i] = clamp_e(a.ids[p < P ? p : P - 1]);
     }
-    for (int i = tid; i < E * W; i += kSortThreads) sh[i] = 0u;
+    for (int i = tid; i < E * WS; i += kSortThreads) sh[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSortPairsPerThread; ++i) {
         const int p = tid + kSortThreads * i;
         if (p < P) {
             const int t = p / K;
-            atomicOr(&sh[eid[i] * W + (t >> 5)], 1u << (t & 31));
+            atomicOr(&sh[eid[i] * WS + (t >> 5)], 1u << (t & 31));
         }
     }
     __syncthreads();
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
     // whether it is active; one scan gives offsets (low 16 bits) and slots
     int c = 0;
     if (tid < E)
-        for (int w = 0; w < W; ++w) c += __popc(sh[tid * W + w]);
+        for (int w = 0; w < W; ++w) c += __popc(sh[tid * WS + w]);
     const bool virt = a.shared != 0 && tid == E;
     const int extra = a.shared != 0 ? a.M : 0;
     int total = 0;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
             const int p = tid + kSortThreads * i;
             if (p < P) {
                 const int t = p / K;
-                const uint32_t* mrow = sh + eid[i] * W;
+                const uint32_t* mrow = sh + eid[i] * WS;
                 int rank = __popc(mrow[t >> 5] & ((1u << (t & 31)) - 1u));
                 for (int w = 0; w < (t >> 5); ++w) rank += __popc(mrow[w]);
                 const int pos = pre[eid[i]] + rank;

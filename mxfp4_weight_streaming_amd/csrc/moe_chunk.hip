@@ -14,7 +14,7 @@ size_t sort_lds_bytes(int M, int K, int E)
     const int P = M * K;
     int NP = 64;
     while (NP < P) NP <<= 1;
-    const size_t mask_words = (size_t)E * ((M + 31) / 32);
+    const size_t mask_words = (size_t)E * (((M + 31) / 32) | 1);   // odd row stride (sort_pairs_kernel)
     return 4 * (mask_words > (size_t)NP ? mask_words : (size_t)NP);
 }
 
