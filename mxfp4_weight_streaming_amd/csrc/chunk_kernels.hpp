@@ -365,12 +365,12 @@ __global__ __launch_bounds__(kSortThreads) void sort_pairs_kernel(SortArgs a)
 // kBigChunkRows).
 // Its waves split K = H into KSPLIT slices: each wave issues all the weight
 // loads of its slice at once (NJ n-tiles of gate and of up, so one activation
-// operand feeds 2 NJ MFMAs), together with the token ids of every tile of the
-// chunk; the block scales of the workgroup's rows are read with full-width
-// loads into LDS.  The 16-token tiles then run with the next tile's
-// activations loading while the current one is reduced; the slices' partial
-// sums are added in LDS in a fixed wave order, where SiLU(g)*u and the
-// per-token activation scale are applied.
+// operand feeds 2 NJ MFMAs), after the chunk's token ids and before the first
+// tile's activations; the block scales of the workgroup's rows are read with
+// full-width loads into LDS.  The 16-token tiles then run with the next
+// tile's activations loading while the current one is reduced; the slices'
+// partial sums are added in LDS in a fixed wave order, where SiLU(g)*u and
+// the per-token activation scale are applied.
 // ---------------------------------------------------------------------------
 template <int H>
 struct ChunkSplit {
@@ -379,14 +379,6 @@ struct ChunkSplit {
     static constexpr int KQ = KS / KSPLIT;              // k-steps per slice
     static_assert(H % 128 == 0 && KS % KSPLIT == 0, "unsupported H for the chunk gate/up");
 };
-
-// Copies `bytes` (a multiple of 16) from global to LDS with 16-byte loads by
-// the whole workgroup of 256 threads.
-__device__ __forceinline__ void copy_to_lds(uint8_t* dst, const uint8_t* src, int bytes)
-{
-    for (int i = threadIdx.x * 16; i < bytes; i += 256 * 16)
-        *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(src + i);
-}
 
 template <int H, int I>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void chunk_gate_up_kernel(
@@ -415,6 +407,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     // NJ + t is up n-tile t.
     constexpr int BPR = 4 * KQ, RSTR = BPR + 1;         // blocks per slice row; LDS row stride in blocks
     __shared__ u32x4 xpose[4][16 * RSTR];               // per wave: one n-tile being rearranged
+    // Token ids come first, since the first tile's activations need them:
+    // this lane's row of the first tile, and row threadIdx.x of the record
+    // for the table the later tiles read from LDS (a record has at most
+    // kBigChunkRows rows, one per thread; rows past the record repeat its
+    // last row).  The vector-memory counter is in issue order, so the loads
+    // are issued in the order they are waited for: ids, weights, the first
+    // tile's activations, block scales.
+    static_assert(kBigChunkRows == 256, "one token id per thread of the workgroup");
+    __shared__ int tok_lds[kBigChunkRows];
+    auto tok_at = [&](int row) { return a.cp.pair_token[off + (row < n ? row : n - 1)]; };
+    const int tok0 = tok_at(r);
+    const int my_tok = tok_at(threadIdx.x);
     u32x4 raw[2 * NJ][KQ];
 #pragma unroll
     for (int t = 0; t < 2 * NJ; ++t) {
@@ -425,28 +429,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             raw[t][i] = load_stream(reinterpret_cast<const u32x4*>(nt + (size_t)(b / BPR) * (H / 2) + (b % BPR) * 16));
         }
     }
-    // token of this lane's row in tile tt (past the chunk: its last row again)
-    auto tok_of = [&](int tt) {
-        const int row = tt * 16 + r;
-        return a.cp.pair_token[off + (row < n ? row : n - 1)];
-    };
-    const int tok0 = tok_of(0);
-    int tok_next = tok_of(1);
-    const uint8_t* s13e = e == kSharedExpert ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * SROW;
-    copy_to_lds(sc_lds[0], s13e + (size_t)j0 * SROW, kGuRows * SROW);
-    copy_to_lds(sc_lds[1], s13e + (size_t)(I + j0) * SROW, kGuRows * SROW);
+    __builtin_amdgcn_sched_barrier(0);                  // every weight load before the wait for tok0
     u32x4 alo[KQ], ahi[KQ];
     float s_row = 0.0f;
     auto load_tile = [&](int t) {
+        s_row = a.act_s[t];                             // first: in by the time the codes are
         const uint8_t* ar = a.act_q + (size_t)t * H + ks0 * 128 + 16 * g;
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
             alo[q] = *reinterpret_cast<const u32x4*>(ar + q * 128);
             ahi[q] = *reinterpret_cast<const u32x4*>(ar + q * 128 + 64);
         }
-        s_row = a.act_s[t];
     };
     load_tile(tok0);
+    // the block scales of the workgroup's gate and up rows: NSC 16-byte loads
+    // per thread and matrix, stored to LDS after the weights are in
+    constexpr int SCH = kGuRows * SROW / 16, NSC = (SCH + 255) / 256;
+    const uint8_t* s13e = e == kSharedExpert ? a.sh.s13 : a.s13 + (size_t)e * 2 * I * SROW;
+    u32x4 scg[NSC], scu[NSC];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int c = threadIdx.x + 256 * i, ci = c < SCH ? c : SCH - 1;
+        scg[i] = *reinterpret_cast<const u32x4*>(s13e + (size_t)j0 * SROW + 16 * ci);
+        scu[i] = *reinterpret_cast<const u32x4*>(s13e + (size_t)(I + j0) * SROW + 16 * ci);
+    }
+    tok_lds[threadIdx.x] = my_tok;
     // into the operand layout through the wave's LDS area: lane (r, g) of
     // k-step q takes block 4 q + g of row r (the row stride of BPR + 1 blocks
     // keeps the 16 rows of one read on distinct banks)
@@ -468,7 +475,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
         __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();                                     // block scales in LDS
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < SCH) {
+            reinterpret_cast<u32x4*>(sc_lds[0])[c] = scg[i];
+            reinterpret_cast<u32x4*>(sc_lds[1])[c] = scu[i];
+        }
+    }
+    lds_barrier();                                      // block scales and token ids in LDS
     constexpr int NP = (KQ + 3) / 4;                    // packed scale registers per n-tile
     int sg[NJ][NP], su[NJ][NP];
 #pragma unroll
@@ -508,16 +523,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             }
         }
         if (w == 0 && g == 0) tok_scale[r] = s_row;
-        // the token ids two tiles ahead, then the next tile's activations (its
-        // ids loaded a tile ago), all in flight while this tile is reduced
-        const int tok_after = tok_of(tile + 2);
-        if (tile + 1 < ntiles) load_tile(tok_next);
-        tok_next = tok_after;
-        __syncthreads();
-        // thread (ii, l) finalises C[4 (l >> 4) + ii][l & 15] of each n-tile
+        // the next tile's activations, in flight while this tile is reduced
+        if (tile + 1 < ntiles) load_tile(tok_lds[(tile + 1) * 16 + r]);
+        lds_barrier();                                  // the loads and stores in flight stay so
+        // thread (ii, l) finalises C[4 (l >> 4) + ii][l & 15] of each n-tile.
+        // A row past the record ran on row n - 1's token (tok_of), so its
+        // value is row n - 1's, bit for bit, and is stored there: the stores
+        // are then unconditional, and the next tile's wait for its operands
+        // counts them exactly instead of waiting for every store in flight.
         const int l = threadIdx.x & 63, ii = threadIdx.x >> 6;
         const int trow = 4 * (l >> 4) + ii;
         const int row = tile * 16 + trow;
+        const int srow = row < n ? row : n - 1;
         const float sc = tok_scale[trow];
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
@@ -527,12 +544,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
                 gs += red[v][nj][0][ii][l];
                 us += red[v][nj][1][ii][l];
             }
-            if (row < n) {
-                const float gv = gs * sc, uv = us * sc;
-                a.h[(size_t)(off + row) * I + j0 + 16 * nj + (l & 15)] = gv / (1.0f + expf(-gv)) * uv;
-            }
+            const float gv = gs * sc, uv = us * sc;
+            a.h[(size_t)(off + srow) * I + j0 + 16 * nj + (l & 15)] = gv / (1.0f + expf(-gv)) * uv;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -561,6 +576,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     const int n0 = nq * kDnRows;
     const uint8_t* w2e = e == kSharedExpert ? a.sh.w2 : a.w2 + (size_t)e * H * (I / 2);
     const uint8_t* sw2e = e == kSharedExpert ? a.sh.s2 : a.sw2 + (size_t)e * H * SROW;
+    // The intermediate row of record row `row` (rows past the record repeat
+    // its last row): its position, or by pair its source pair, which comes
+    // from memory; the later tiles read those from a table in LDS (a record
+    // has at most kBigChunkRows rows, one per thread).  The vector-memory
+    // counter is in issue order, so the loads are issued in the order they
+    // are waited for: (by pair) the first tile's rows, weights, the first
+    // tile's activations, block scales.
+    static_assert(kBigChunkRows == 256, "one source row per thread of the workgroup");
+    __shared__ int src_lds[BY_PAIR ? kBigChunkRows : 1];
+    auto src_at = [&](int row) {
+        const int pos = off + (row < n ? row : n - 1);
+        return BY_PAIR ? a.cp.pair_src[pos] : pos;
+    };
+    auto src_row = [&](int row) {                       // rows below kBigChunkRows
+        if constexpr (BY_PAIR) return src_lds[row];
+        else return off + (row < n ? row : n - 1);
+    };
+    int arow0 = src_at(r), erow0[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) erow0[i] = src_at(4 * g + i);
+    const int my_src = BY_PAIR ? src_at(threadIdx.x) : 0;
     // A row is BPR 16-byte blocks (one E8M0 block each) and an n-tile's 16
     // rows are one contiguous run of 16 BPR blocks: load i of lane l fetches
     // block 64 i + l of it (the gate/up kernel's scheme; the operand layout
@@ -577,17 +613,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             raw[nj][i] = load_stream(reinterpret_cast<const u32x4*>(nt + (size_t)(b < NBLK ? b : NBLK - 1) * 16));
         }
     }
-    if constexpr (SBYTES % 16 == 0) {
-        copy_to_lds(sc_lds, sw2e + (size_t)n0 * SROW, SBYTES);
-    } else {
-        for (int i = threadIdx.x; i < SBYTES; i += 256) sc_lds[i] = sw2e[(size_t)n0 * SROW + i];
-    }
+    __builtin_amdgcn_sched_barrier(0);                  // every weight load before the first wait
     u32x4 alo[KS], ahi[KS];
     float es[4];                                          // s2 of the rows this lane stores
-    auto load_tile = [&](int base) {
-        const int row = base + r;
-        const int pos = off + (row < n ? row : n - 1);
-        const int arow = BY_PAIR ? a.cp.pair_src[pos] : pos;
+    auto load_tile = [&](int arow, const int (&erow)[4]) {
         const uint8_t* q = a.q2 + (size_t)arow * I + 16 * g;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -602,13 +631,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row2 = base + 4 * g + i;
-            const int pos2 = off + (row2 < n ? row2 : n - 1);
-            es[i] = a.s2[BY_PAIR ? a.cp.pair_src[pos2] : pos2];
-        }
+        for (int i = 0; i < 4; ++i) es[i] = a.s2[erow[i]];
     };
-    load_tile(0);
+    load_tile(arow0, erow0);
+    // the block scales of the workgroup's rows: NSC 16-byte loads per thread,
+    // stored to LDS after the weights are in
+    static_assert(SBYTES % 16 == 0, "block scales in 16-byte loads");
+    constexpr int SCH = SBYTES / 16, NSC = (SCH + 255) / 256;
+    u32x4 scv[NSC];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        scv[i] = *reinterpret_cast<const u32x4*>(sw2e + (size_t)n0 * SROW + 16 * (c < SCH ? c : SCH - 1));
+    }
+    if constexpr (BY_PAIR) src_lds[threadIdx.x] = my_src;
     // into the operand layout through the wave's LDS area: lane (r, g) of
     // k-step ks takes block 4 ks + g of row r, zero codes past the row
     i32x8 b[NJ][KS];
@@ -633,7 +669,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();                                      // block scales in LDS
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < SCH) reinterpret_cast<u32x4*>(sc_lds)[c] = scv[i];
+    }
+    lds_barrier();                                        // block scales (and source rows) in LDS
     constexpr int NP = (KS + 3) / 4;                    // packed scale registers per n-tile
     int sc[NJ][NP];
 #pragma unroll
@@ -660,15 +701,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         float esc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) esc[i] = es[i];
-        if (base + 16 < n) load_tile(base + 16);
+        if (base + 16 < n) {
+            int erow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) erow[i] = src_row(base + 16 + 4 * g + i);
+            load_tile(src_row(base + 16 + r), erow);
+        }
+        // A row past the record ran on row n - 1's activations and scale, so
+        // its value is row n - 1's, bit for bit, and is stored there: the
+        // stores are then unconditional, and the next tile's wait for its
+        // operands counts them exactly instead of waiting for every store.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row2 = base + 4 * g + i;
-            if (row2 < n) {
-                float* yr = a.y + (size_t)(off + row2) * H + n0 + w * NJ * 16 + r;
+            float* yr = a.y + (size_t)(off + (row2 < n ? row2 : n - 1)) * H + n0 + w * NJ * 16 + r;
 #pragma unroll
-                for (int nj = 0; nj < NJ; ++nj) yr[16 * nj] = acc[nj][i] * esc[i];
-            }
+            for (int nj = 0; nj < NJ; ++nj) yr[16 * nj] = acc[nj][i] * esc[i];
         }
     }
 }

@@ -150,6 +150,18 @@ __device__ __forceinline__ T load_stream(const T* p)
     return __builtin_nontemporal_load(p);   // weights are read once per call
 }
 
+// Workgroup barrier for data handed over in LDS only.  __syncthreads also
+// releases global memory: with a global store in flight it waits for the
+// whole vector-memory counter, which on gfx950 counts loads and stores in
+// issue order, so it waits for every load in flight as well (the next tile's
+// operands, say).  Here only this wave's LDS operations are waited for.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Cross-lane helpers on DPP (no LDS round trip): four steps reduce each row of
 // 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
 // results are read as scalars and combined in a fixed order, so every lane
