@@ -170,9 +170,10 @@ __global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
 // pair's rank inside its expert is a popcount of the mask below its token.
 // A token naming an expert more than once shows as a popcount total below
 // M*K; such ids take exact counts and a bitonic sort of (expert << 16 | pair)
-// keys.  The rows of every slot are then cut into chunks of at most
-// kChunkRows rows for the grouped kernels, 4-tile chunks first, then 3-, 2-
-// and 1-tile ones.
+// keys.  The rows of every slot are then cut into chunk records for the
+// grouped kernels: a busy expert's (more than kChunkRows rows) first, cut
+// evenly into records of at most kBigChunkRows rows, then the others as one
+// record each, 4-tile records before 3-, 2- and 1-tile ones.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 constexpr int kSortPairsPerThread = kMaxChunkPairs / kSortThreads;

@@ -32,12 +32,36 @@ KERNEL_SOURCES = ["mxfp4_weight_streaming_amd/csrc/gemv_kernels.hpp",
                   "mxfp4_weight_streaming_amd/csrc/topk_wave.hpp"]
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed:
+    what the compiler sees, so that a comment edit keeps a kernel's counters
+    valid while any change to its code invalidates them.  (The kernel sources
+    hold no string or character literals containing comment markers.)"""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def _sources_hash(paths) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
+
+
+def kernel_source_hash() -> str:
+    return _sources_hash(KERNEL_SOURCES)
 
 
 def _short(name: str) -> str:
@@ -168,11 +192,7 @@ CHUNK_SOURCES = ["mxfp4_weight_streaming_amd/csrc/chunk_kernels.hpp",
 
 
 def chunk_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in CHUNK_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    return _sources_hash(CHUNK_SOURCES)
 
 
 def mfma(counters_csv: str, out_path: str, command: str, xcds: int, simds: int, alg_flops) -> None:
