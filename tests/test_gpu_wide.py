@@ -5,7 +5,8 @@ verify windows), against the CPU oracle through the C ABI.
 Routing (P2 and the bit-exact compaction) is checked for every token; the
 layer output (P5) for every token up to 4 tokens (the verify window), and for
 the first and last token of larger calls, since a token's output depends only
-on that token and the oracle takes ~1.4 s per token here.
+on that token and the oracle takes ~1.4 s per token here.  At 512 experts
+the chunk path (100 and 2048 tokens) is checked the same way.
 """
 import numpy as np
 import pytest
@@ -40,7 +41,7 @@ def _route_and_layer(moe, w, dw, M, seed):
     K = 8
     li = synth.decode_tokens(seed, w, M, K=K)
     shp = moe.shape(w.H, w.I, w.E, K)
-    ws = moe.workspace(shp, 8)
+    ws = moe.workspace(shp, max(M, 8))
     S = min(w.E, M * K)
     ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
     wts = torch.empty((M, K), dtype=torch.float32, device="cuda")
@@ -87,6 +88,16 @@ def test_ling_512_experts(moe, ling512, M):
     w, dw = ling512
     n = _route_and_layer(moe, w, dw, M, seed=300 + M)
     assert n <= min(512, 8 * M)
+
+
+@pytest.mark.parametrize("M", [100, 2048])
+def test_ling_512_experts_chunk_path(moe, ling512, M):
+    """512 experts through the chunk path (more than 8 tokens); at 2048 tokens
+    the pair sort keeps 512 token masks of 65 words in LDS (133 KB, its
+    largest case)."""
+    w, dw = ling512
+    n = _route_and_layer(moe, w, dw, M, seed=340 + M)
+    assert n <= 512
 
 
 @pytest.mark.parametrize("M", [2, 3, 5, 6, 7, 8])
