@@ -101,8 +101,10 @@ def test_shared_tiny_decode(moe, M):
     _check_layer(moe, shp, x, w, dw, sh, dsh, moe.workspace(shp, 8), chunk=False)
 
 
-@pytest.mark.parametrize("M", [9, 61, 200])
+@pytest.mark.parametrize("M", [9, 61, 200, 600, 2048])
 def test_shared_tiny_chunk(moe, M):
+    """Up to 2048 tokens: the shared expert's M rows are then cut into several
+    chunk records of at most 256 rows (3 at 600 tokens, 8 at 2048)."""
     w, dw, sh, dsh = _tiny(80 + M)
     shp = moe.shape(256, 64, 16, 2)
     x = synth.decode_tokens(90 + M, w, M, K=2).x
