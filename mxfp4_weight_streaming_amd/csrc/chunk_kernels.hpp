@@ -11,14 +11,17 @@
 // in the combine.  The
 // pages profile MoE decode as bound by reading expert weights ([EN] "Why is
 // MoE decoding on DGX Spark memory-bound?"); here too each weight byte is read
-// from HBM once per call, by the wave that owns its 16 rows.
+// from HBM once per chunk record, by the wave that owns its 16 rows (an expert
+// has one record, or several of up to 256 rows when more rows picked it).
 //
 // A chunk is eight kernels on one stream:
 //   chunk_router_kernel   bf16 MFMA router GEMM, fp32 logits
 //   quant_kernel          per-token FP8 activations (shared with the decode path)
 //   chunk_topk_kernel     one wave per token: top-K and renormalised weights
-//   sort_pairs_kernel     one workgroup: (expert, pair) bitonic sort in LDS ->
-//                         active experts, per-expert offsets, pair lists
+//   sort_pairs_kernel     one workgroup: token bitmasks per expert in LDS,
+//                         ranks by popcount (a bitonic sort when a token names
+//                         an expert twice) -> active experts, per-expert
+//                         offsets, pair lists, chunk records
 //   chunk_gate_up_kernel  per (expert, 32 intermediate rows): gate and up
 //                         tiles on MFMA, K split over the workgroup's waves,
 //                         SiLU(gate)*up epilogue -> h fp32
