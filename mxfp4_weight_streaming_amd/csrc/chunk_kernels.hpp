@@ -14,10 +14,11 @@
 // from HBM once per chunk record, by the wave that owns its 16 rows (an expert
 // has one record, or several of up to 256 rows when more rows picked it).
 //
-// A chunk is eight kernels on one stream:
+// A chunk is seven kernels on one stream:
 //   chunk_router_kernel   bf16 MFMA router GEMM, fp32 logits
-//   quant_kernel          per-token FP8 activations (shared with the decode path)
-//   chunk_topk_kernel     one wave per token: top-K and renormalised weights
+//   chunk_topk_kernel     one wave per token: top-K and renormalised weights,
+//                         and the token's per-token FP8 activations (for
+//                         H > 4096 those come from quant_kernel, run before)
 //   sort_pairs_kernel     one workgroup: token bitmasks per expert in LDS,
 //                         ranks by popcount (a bitonic sort when a token names
 //                         an expert twice) -> active experts, per-expert
@@ -155,13 +156,73 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void chunk_router_kernel(Chun
 }
 
 // ---------------------------------------------------------------------------
-// Top-K and weights, one wave per token.
+// Top-K and weights, one wave per token; with act_q, the token's FP8
+// activations too.  The token's logits are requested first and its
+// activations next, so the activations arrive during the top-K rounds (the
+// top-K is inlined here: a call would wait for every load in flight).  The
+// quantisation is quant_kernel's: s = amax / 448 over the token's row (one
+// wave holds the whole row; a maximum is exact in any order), codes
+// E4M3(x / s) with the correctly rounded quotient.
 // ---------------------------------------------------------------------------
+template <int PER, bool QUANT>
+__device__ __forceinline__ void topk_quant_token(const ChunkTopkArgs& a, int t)
+{
+    constexpr int NQ = kTopkQuantMaxH / 8 / kWave;      // 16-byte chunks of the row per lane
+    const int lane = threadIdx.x & 63;
+    const __attribute__((address_space(1))) float* L =
+        (const __attribute__((address_space(1))) float*)(a.logits + (size_t)t * a.E);
+    uint32_t u[PER];
+    int sl[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + kWave * i;
+        u[i] = topk_key(L[e < a.E ? e : a.E - 1], e < a.E);
+        sl[i] = i;
+    }
+    const int nc8 = a.H / 8;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+    u32x4 xv[NQ];
+    if constexpr (QUANT) {
+        __builtin_amdgcn_sched_barrier(0);              // the logits first: the top-K waits only for them
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) xv[i] = xr[min(lane + kWave * i, nc8 - 1)];   // clamped: no branch
+    }
+    topk_select_t<PER>(u, sl, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K, a.K);
+    if constexpr (!QUANT) return;
+    auto bf = [](uint32_t v, int hi) { return __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16)); };
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        if (lane + kWave * i < nc8) {
+            const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(bf(vv[j >> 1], j & 1)));
+        }
+    }
+    const QuantScale qs = quant_scale(wave_max(m));
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int c = lane + kWave * i;
+        if (c < nc8) {
+            const uint32_t vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            uint32_t code[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) code[j >> 2] |= e4m3_encode(quant_div(bf(vv[j >> 1], j & 1), qs)) << (8 * (j & 3));
+            *reinterpret_cast<u32x2*>(a.act_q + (size_t)t * a.H + 8 * c) = u32x2{code[0], code[1]};
+        }
+    }
+    if (lane == 0) a.act_s[t] = qs.s;
+}
+
+template <bool QUANT>
 __global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.M) return;                              // whole wave; no barrier follows
-    topk_wave(a.logits + (size_t)t * a.E, a.E, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K);
+    if (a.E <= 64) topk_quant_token<1, QUANT>(a, t);
+    else if (a.E <= 128) topk_quant_token<2, QUANT>(a, t);
+    else if (a.E <= 256) topk_quant_token<4, QUANT>(a, t);
+    else topk_quant_token<8, QUANT>(a, t);
 }
 
 // ---------------------------------------------------------------------------

@@ -219,9 +219,19 @@ moe_status enqueue_quant(const moe_shape* s, int32_t M, const uint16_t* x, uint8
     return e == hipSuccess ? MOE_OK : hip_fail(e, "quant launch");
 }
 
-moe_status enqueue_chunk_topk(const moe_shape* s, int32_t M, int32_t* ids, float* w, const Carved& c, hipStream_t st)
+// Top-K of a chunk; with act_q, the tokens' FP8 quantisation in the same
+// kernel where a wave holds a token's row (H <= kTopkQuantMaxH), otherwise
+// in quant_kernel before it.
+moe_status enqueue_chunk_topk(const moe_shape* s, int32_t M, int32_t* ids, float* w, const Carved& c, hipStream_t st,
+                              const uint16_t* x = nullptr, uint8_t* act_q = nullptr, float* act_s = nullptr)
 {
-    moe::ChunkTopkArgs a{c.at<float>(c.L.logits), M, s->num_experts, s->topk, ids, w};
+    const bool fused = act_q != nullptr && s->hidden <= moe::kTopkQuantMaxH;
+    if (act_q != nullptr && !fused) {
+        const hipError_t e = moe::launch_quant(s->hidden, x, M, act_q, act_s, st);
+        if (e != hipSuccess) return hip_fail(e, "quant launch");
+    }
+    moe::ChunkTopkArgs a{c.at<float>(c.L.logits), M, s->num_experts, s->topk, ids, w,
+                         x, s->hidden, fused ? act_q : nullptr, act_s};
     hipError_t e = moe::launch_chunk_topk(a, st);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "chunk topk launch");
 }
@@ -374,8 +384,7 @@ moe_status decode_forward(const moe_shape* shape, int32_t M, const uint16_t* hid
     }
     if (chunked(M)) {
         if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s, ev(0))) != MOE_OK) return st;
-        if ((st = enqueue_quant(shape, M, hidden, q, sc, s)) != MOE_OK) return st;
-        if ((st = enqueue_chunk_topk(shape, M, ids, w, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_topk(shape, M, ids, w, c, s, hidden, q, sc)) != MOE_OK) return st;
         if ((st = enqueue_sort(shape, M, ids, c, s, has_shared(sh))) != MOE_OK) return st;
         return enqueue_chunk_experts(shape, M, q, sc, w, w13, w13_scale, w2, w2_scale, out, c, s, ev(1), ev(2), sh);
     }
@@ -568,8 +577,7 @@ moe_status moe_route(const moe_shape* shape, int32_t M, const uint16_t* hidden, 
         return fail(MOE_ERR_INVALID_ARG, "taps act_fp8 and act_scale must be given together");
     if (chunked(M)) {
         if ((st = enqueue_chunk_router(shape, M, hidden, router_w, c, s)) != MOE_OK) return st;
-        if (act_q != nullptr && (st = enqueue_quant(shape, M, hidden, act_q, act_s, s)) != MOE_OK) return st;
-        if ((st = enqueue_chunk_topk(shape, M, topk_ids, topk_w, c, s)) != MOE_OK) return st;
+        if ((st = enqueue_chunk_topk(shape, M, topk_ids, topk_w, c, s, hidden, act_q, act_s)) != MOE_OK) return st;
         if ((st = enqueue_sort(shape, M, topk_ids, c, s)) != MOE_OK) return st;
     } else {
         if ((st = enqueue_router(shape, M, hidden, router_w, act_q, act_s, c, s)) != MOE_OK) return st;

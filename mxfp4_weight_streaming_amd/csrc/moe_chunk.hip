@@ -61,7 +61,11 @@ hipError_t launch_chunk_router(int H, const ChunkRouterArgs& a, hipStream_t s, c
 
 hipError_t launch_chunk_topk(const ChunkTopkArgs& a, hipStream_t s, const LaunchEvents& ev)
 {
-    return launch(chunk_topk_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, ev, a);
+    if (a.act_q != nullptr) {
+        if (a.H > kTopkQuantMaxH || a.H % 8 != 0) return hipErrorInvalidValue;
+        return launch(chunk_topk_kernel<true>, dim3((a.M + 3) / 4), dim3(256), 0, s, ev, a);
+    }
+    return launch(chunk_topk_kernel<false>, dim3((a.M + 3) / 4), dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_sort_pairs(const SortArgs& a, hipStream_t s, const LaunchEvents& ev)
@@ -115,11 +119,12 @@ void chunk_kernel_names(int H, int I, char* buf, size_t n)
 {
     const Kern k = find_kernel(key_chunk_gate_up(H, I));
     snprintf(buf, n,
-             "chunk_router_kernel<H=%d> (bf16 MFMA 16x16x32) -> quant_kernel<%d> -> chunk_topk_kernel -> "
+             "chunk_router_kernel<H=%d> (bf16 MFMA 16x16x32) -> %s -> "
              "sort_pairs_kernel (1 workgroup: token bitmasks in LDS) -> chunk_gate_up_kernel<%d,%d> (scaled FP8xFP4 "
              "MFMA 16x16x128, %d workgroups per 64-token chunk, K split over %d waves) -> requant_kernel<%d> -> "
              "chunk_down_kernel<%d,%d> (scaled FP8xFP4 MFMA, %d workgroups per chunk) -> combine_kernel<%d>%s",
-             H, H, H, I, I / kGuRows, chunk_k_split(H), I, H, I, H / kDnRows, H,
+             H, H <= kTopkQuantMaxH ? "chunk_topk_kernel (top-K + FP8 quantisation)" : "quant_kernel -> chunk_topk_kernel",
+             H, I, I / kGuRows, chunk_k_split(H), I, H, I, H / kDnRows, H,
              k.jit != nullptr ? " [compiled at run time]" : "");
 }
 

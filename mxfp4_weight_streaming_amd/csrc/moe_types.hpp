@@ -116,11 +116,18 @@ struct ChunkRouterArgs {
     float* logits;         // [M,E]
 };
 
+// Chunk top-K, and with act_q the tokens' FP8 quantisation too (a token's
+// wave holds its whole row: H <= kTopkQuantMaxH).
+constexpr int kTopkQuantMaxH = 4096;
 struct ChunkTopkArgs {
     const float* logits;   // [M,E]
     int M, E, K;
     int32_t* ids;          // [M,K]
     float* w;              // [M,K]
+    const uint16_t* x;     // [M,H] bf16 hidden states (read only with act_q)
+    int H;
+    uint8_t* act_q;        // [M,H] E4M3 codes, or null: no quantisation here
+    float* act_s;          // [M] scales
 };
 
 // Work list of the grouped kernels: the sorted rows of each active expert
