@@ -56,13 +56,98 @@ struct TopkRanks {
     uint32_t top;
 };
 
-// The R rounds on keys already held by the lanes: lane l holds the keys of
-// experts l + 64 i in u[i] (0 for experts past E), s[i] = i.  Sorts each
-// lane's entries first.
+// Selection by threshold, one pass.  The lanes form 8 groups of 8 (lanes
+// 8g..8g+7, all their entries); each group's largest key is an entry of its
+// own, so at least 8 entries are >= T, the smallest of the 8 group maxima, and
+// the K <= 8 selected entries (whose keys are >= the K-th largest) are among
+// the candidates, the valid entries with key >= T.  The candidates go to LDS
+// as 64-bit keys (key << 32 | 0xFFFF - expert: distinct, and larger exactly
+// when the logit is larger or, for an equal logit, the expert lower), and each
+// candidate's rank is the number of larger candidate keys.  That is the
+// canonical order of the rounds below, so both give the same ranks.  Returns
+// false, having written nothing, when the candidates do not fit one per lane
+// (many equal logits) or are fewer than R; the caller then takes the rounds.
+constexpr int kTopkMaxWaves = 16;               // waves in a workgroup of 1024 threads
+
+// This wave's LDS area of the threshold pass: one array for every caller and
+// instantiation (a kernel holds it once).
+__device__ __forceinline__ uint64_t* topk_lds_wave()
+{
+    __shared__ __attribute__((aligned(16))) uint64_t tk_lds[kTopkMaxWaves][kWave + kMaxTopK];
+    return tk_lds[threadIdx.x >> 6];
+}
+
 template <int PER>
+__device__ __forceinline__ bool topk_threshold_t(const uint32_t (&u)[PER], const int (&s)[PER], int R,
+                                                 TopkRanks& out)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t* c = topk_lds_wave();
+    uint32_t g = u[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) g = max(g, u[i]);
+    g = max(g, dpp_u32<kDppXor1>(g));            // the maximum of each group of 8 lanes
+    g = max(g, dpp_u32<kDppXor2>(g));
+    g = max(g, dpp_u32<kDppHalfMirror>(g));
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)g, 0), top = lo;
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)g, 8 * q);
+        lo = min(lo, v);
+        top = max(top, v);
+    }
+    const uint32_t thr = max(lo, 1u);            // key 0 marks entries past E
+    uint64_t b[PER];
+    int nc = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        b[i] = __ballot(u[i] >= thr);
+        nc += __popcll(b[i]);
+    }
+    if (nc > kWave || nc < R) return false;
+    c[lane] = 0;                                 // entries past the candidates rank below all
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (u[i] >= thr) {
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b[i] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)b[i], 0u));
+            c[pos] = ((uint64_t)u[i] << 32) | (uint32_t)(0xFFFF - (lane + kWave * s[i]));
+        }
+        base += __popcll(b[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = c[lane];
+    int rank = 0;
+    for (int j = 0; j < nc; j += 4) {            // the same addresses in every lane: broadcast reads
+        const ulonglong2 k01 = *reinterpret_cast<const ulonglong2*>(c + j);
+        const ulonglong2 k23 = *reinterpret_cast<const ulonglong2*>(c + j + 2);
+        rank += (k01.x > mine) + (k01.y > mine) + (k23.x > mine) + (k23.y > mine);
+    }
+    if (lane < nc && rank < R) c[kWave + rank] = mine;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t k = c[kWave + min(lane, kMaxTopK - 1)];
+    const bool ranked = lane < R;
+    out.e = ranked ? (int)(0xFFFFu - (uint32_t)(k & 0xFFFFu)) : 0;
+    out.u = ranked ? (uint32_t)(k >> 32) : 0u;
+    out.top = top;
+    return true;
+}
+
+// The R rounds on keys already held by the lanes: lane l holds the keys of
+// experts l + 64 s[i] in u[i] (0 for experts past E), s[i] = i.  With THRESH
+// the threshold pass above serves whenever it can; the rounds sort each lane's
+// entries first.
+template <int PER, bool THRESH = true>
 __device__ __forceinline__ TopkRanks topk_rounds_t(uint32_t (&u)[PER], int (&s)[PER], int R)
 {
     const int lane = threadIdx.x & 63;
+    if constexpr (THRESH) {
+        TopkRanks t;
+        if (topk_threshold_t<PER>(u, s, R, t)) return t;
+    }
     // sorting network over the lane's entries (a strict order: slots differ)
     if constexpr (PER == 2) {
         lane_sort_step<PER>(u, s, 0, 1);
@@ -169,7 +254,10 @@ __device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t*
 }
 
 // The first R ranks of one token's E logits by one wave, in registers (see
-// TopkRanks).  Inlined: its callers keep the result in registers.
+// TopkRanks).  Inlined: its callers keep the result in registers.  By the
+// rounds only: it serves one token in the gate/up kernel, where the threshold
+// pass made the graph-replayed one-token layer slower (16.2 -> 16.4 us per
+// layer, same box) although the kernel alone was no slower.
 template <int PER>
 __device__ __forceinline__ TopkRanks topk_ranks_t(const float* Lg, int E, int R)
 {
@@ -183,7 +271,7 @@ __device__ __forceinline__ TopkRanks topk_ranks_t(const float* Lg, int E, int R)
         u[i] = topk_key(L[e < E ? e : E - 1], e < E);
         s[i] = i;
     }
-    return topk_rounds_t<PER>(u, s, R);
+    return topk_rounds_t<PER, false>(u, s, R);
 }
 
 // topk_ranks_t with the logits-per-lane count chosen by E (wave-uniform).
