@@ -250,7 +250,7 @@ def phases(trace_csv: str, out_path: str, kernel_prefix: str, sizes, names) -> N
     last_end = 0
     for r in every:
         s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        if r["Kernel_Name"].startswith(kernel_prefix):
+        if _short(r["Kernel_Name"]).startswith(_short(kernel_prefix)):   # with or without "void "
             raw.append((e - s) / 1e3)
             excl.append((e - max(s, last_end)) / 1e3)
             early.append(s < last_end)
