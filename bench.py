@@ -200,7 +200,12 @@ def main() -> int:
         "roofline": {"kernel": rl["kernel"], "bound": "hbm", "achieved": round(rl["gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rl["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": rl["bytes"], "us_per_launch": round(rl["us"], 3),
-                     "timing": rl["timing"]},
+                     "timing": rl["timing"],
+                     # the headline's own launch mode (graph replay) leaves gate/up the layer's time
+                     # less the other two kernels' launch-stamped times: the same within a few %
+                     "graph_layer_less_router_and_down_us": (
+                         round(head["us_per_layer"] - head["kernel_us"]["router"] - head["kernel_us"]["down"], 3)
+                         if "router" in head["kernel_us"] else None)},
         "shared_expert": {"by_tokens": {n: r["shared"] for n, r in results.items() if r.get("shared")}} or None,
         "chunk": chunk,
         "lm_head": lm_head,
