@@ -2,6 +2,8 @@
 // lm_head_kernels.hpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernel_table.hpp"
 #include "lm_head_kernels.hpp"
 #include "moe_internal.hpp"
@@ -32,8 +34,18 @@ hipError_t launch_lm_head_gemv(int H, int mt, const uint16_t* x, int M, const ui
 {
     const Kern k = find_kernel(key_lm_head(H, mt));
     if (!k.ok()) return hipErrorInvalidDeviceFunction;
-    const int blocks = (V + 15) / 16;
-    const int grid = blocks < 1024 ? blocks : 1024;      // four workgroups per CU, striding over row blocks
+    // as many workgroups as are resident at once (every one striding over the
+    // row blocks): a workgroup queued behind a full compute unit would start
+    // only when another ends, and the last ones would run alone
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = k.aot != nullptr ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.aot, 256, 0)
+                             : hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.jit, 256, 0);
+    if (e != hipSuccess) return e;
+    const int blocks = (V + 15) / 16, resident = std::max(per_cu, 1) * std::max(cus, 1);
+    const int grid = blocks < resident ? blocks : resident;
     return launch_kern(k, dim3(grid), dim3(256), 0, s, {}, x, M, q, scale, V, logits);
 }
 

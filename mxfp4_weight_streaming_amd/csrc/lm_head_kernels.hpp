@@ -79,6 +79,18 @@ __device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
+// Row blocks per unrolled round of the GEMV loop (even: the stage a round's
+// last look-ahead fills is the one its next round starts on).  Inside a round
+// the two stages are never carried around a loop edge; a rolled loop did carry
+// them, and the compiler then waited for every load in flight at its head, so
+// each workgroup had one block in flight instead of two.
+__host__ __device__ constexpr int lm_head_blocks_per_round(int mt) { return mt <= 4 ? 8 : 4; }
+
+// (The compiler unrolls each round of the loop below, NB bodies with exact
+// waits, yet reports a loop transformation it did not perform; that warning
+// is silenced for this kernel.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wpass-failed"
 template <int H, int MT>
 __global__ __launch_bounds__(256) void lm_head_gemv_kernel(const uint16_t* __restrict__ x, int M,
                                                            const uint8_t* __restrict__ q,
@@ -86,30 +98,41 @@ __global__ __launch_bounds__(256) void lm_head_gemv_kernel(const uint16_t* __res
                                                            float* __restrict__ logits)
 {
     constexpr int LPR = 16, CPL = H / 16 / LPR;        // 16-code chunks per lane
+    constexpr int NB = lm_head_blocks_per_round(MT);
+    static_assert(NB % 2 == 0, "a round ends on the stage the next one starts with");
     static_assert(H % (16 * LPR) == 0, "LM-head GEMV needs H % 256 == 0");
     __shared__ u32x4 xs[MT * H / 8];                    // [token][8-element group] of bf16
     for (int i = threadIdx.x; i < M * H / 8; i += 256) xs[i] = reinterpret_cast<const u32x4*>(x)[i];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane % LPR, grp = lane / LPR;
     const int blocks = (V + 15) / 16;
-    auto load = [&](int blk, u32x4* wv) {
-        const int v = min(blk * 16 + wave * 4 + grp, V - 1);
-        const u32x4* row = reinterpret_cast<const u32x4*>(q + (size_t)v * H);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) wv[i] = load_stream(row + li + LPR * i);
+    struct Stage {
+        u32x4 w[CPL];
+        float sc;                                       // the row's scale, loaded with its codes
     };
-    int blk = blockIdx.x;
-    if (blk >= blocks) return;
-    u32x4 w0[CPL], w1[CPL];
-    load(blk, w0);
+    // dummy: the look-ahead past the workgroup's last block.  Its loads are
+    // still issued, so that every wait covers exactly the block in use, but
+    // all at the first 16 bytes of the head (one line per instruction).
+    auto load = [&](int blk, Stage& st, bool dummy) {
+        const int v = dummy ? 0 : min(blk * 16 + wave * 4 + grp, V - 1);
+        const u32x4* row = reinterpret_cast<const u32x4*>(q + (size_t)v * H);
+        const int lo = dummy ? 0 : li, step = dummy ? 0 : LPR;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) st.w[i] = load_stream(row + lo + step * i);
+        st.sc = scale[v];
+    };
+    const int blk0 = blockIdx.x;
+    if (blk0 >= blocks) return;
+    Stage st[2];
+    load(blk0, st[0], false);
     __syncthreads();                                    // activations staged
-    auto compute = [&](int b, const u32x4* wv) {
+    auto compute = [&](int b, const Stage& sg) {
         float acc[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = li + LPR * i;                 // 16 codes = elements 16c .. 16c+15
-            const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+            const uint32_t d[4] = {sg.w[i].x, sg.w[i].y, sg.w[i].z, sg.w[i].w};
             uint32_t wb[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -138,22 +161,24 @@ __global__ __launch_bounds__(256) void lm_head_gemv_kernel(const uint16_t* __res
         for (int t = 0; t < MT; ++t) {
             if (t < M) {
                 const float sum = group_sum<LPR>(acc[t]);
-                if (li == 0 && v < V) logits[(size_t)t * V + v] = sum * scale[v];
+                if (li == 0 && v < V) logits[(size_t)t * V + v] = sum * sg.sc;
             }
         }
     };
+    // blocks blk0, blk0 + grid, ...: the next block's loads are issued before
+    // the current one is computed (past the last, a dummy issue, unused)
+    int cur = blk0;
     for (;;) {
-        const int nb = blk + gridDim.x;
-        if (nb < blocks) load(nb, w1);
-        compute(blk, w0);
-        if (nb >= blocks) break;
-        blk = nb;
-        const int nb2 = blk + gridDim.x;
-        if (nb2 < blocks) load(nb2, w0);
-        compute(blk, w1);
-        if (nb2 >= blocks) break;
-        blk = nb2;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (cur >= blocks) return;
+            const int nxt = cur + (int)gridDim.x;
+            load(nxt < blocks ? nxt : cur, st[(k + 1) & 1], nxt >= blocks);
+            compute(cur, st[k & 1]);
+            cur = nxt;
+        }
     }
 }
+#pragma clang diagnostic pop
 
 }  // namespace moe
