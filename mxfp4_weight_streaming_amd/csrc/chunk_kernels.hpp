@@ -158,35 +158,29 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void chunk_router_kernel(Chun
 // ---------------------------------------------------------------------------
 // Top-K and weights, one wave per token; with act_q, the token's FP8
 // activations too.  The token's logits are requested first and its
-// activations next, so the activations arrive during the top-K rounds (the
-// top-K is inlined here: a call would wait for every load in flight).  The
-// quantisation is quant_kernel's: s = amax / 448 over the token's row (one
-// wave holds the whole row; a maximum is exact in any order), codes
-// E4M3(x / s) with the correctly rounded quotient.
+// activations next, so the activations arrive during the top-K rounds; the
+// keys are waited for before the dispatch on E (topk_keys8), the activations
+// only where they are used (the top-K is inlined here: a call would wait for
+// every load in flight).  The quantisation is quant_kernel's: s = amax / 448
+// over the token's row (one wave holds the whole row; a maximum is exact in
+// any order), codes E4M3(x / s) with the correctly rounded quotient.
 // ---------------------------------------------------------------------------
+constexpr int kTopkQuantChunks = kTopkQuantMaxH / 8 / kWave;   // 16-byte chunks of a row per lane
+
 template <int PER, bool QUANT>
-__device__ __forceinline__ void topk_quant_token(const ChunkTopkArgs& a, int t)
+__device__ __forceinline__ void topk_quant_token(const ChunkTopkArgs& a, int t, const TopkKeys8& k,
+                                                 const u32x4 (&xv)[kTopkQuantChunks])
 {
-    constexpr int NQ = kTopkQuantMaxH / 8 / kWave;      // 16-byte chunks of the row per lane
+    constexpr int NQ = kTopkQuantChunks;
     const int lane = threadIdx.x & 63;
-    const __attribute__((address_space(1))) float* L =
-        (const __attribute__((address_space(1))) float*)(a.logits + (size_t)t * a.E);
     uint32_t u[PER];
     int sl[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = lane + kWave * i;
-        u[i] = topk_key(L[e < a.E ? e : a.E - 1], e < a.E);
+        u[i] = k.u[i];
         sl[i] = i;
     }
     const int nc8 = a.H / 8;
-    const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
-    u32x4 xv[NQ];
-    if constexpr (QUANT) {
-        __builtin_amdgcn_sched_barrier(0);              // the logits first: the top-K waits only for them
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) xv[i] = xr[min(lane + kWave * i, nc8 - 1)];   // clamped: no branch
-    }
     topk_select_t<PER>(u, sl, a.K, a.ids + (size_t)t * a.K, a.w + (size_t)t * a.K, a.K);
     if constexpr (!QUANT) return;
     auto bf = [](uint32_t v, int hi) { return __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16)); };
@@ -219,10 +213,21 @@ __global__ __launch_bounds__(256) void chunk_topk_kernel(ChunkTopkArgs a)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.M) return;                              // whole wave; no barrier follows
-    if (a.E <= 64) topk_quant_token<1, QUANT>(a, t);
-    else if (a.E <= 128) topk_quant_token<2, QUANT>(a, t);
-    else if (a.E <= 256) topk_quant_token<4, QUANT>(a, t);
-    else topk_quant_token<8, QUANT>(a, t);
+    const int lane = threadIdx.x & 63;
+    const TopkLogits8 lg = topk_load_logits8(a.logits + (size_t)t * a.E, a.E);
+    u32x4 xv[kTopkQuantChunks];
+    if constexpr (QUANT) {
+        __builtin_amdgcn_sched_barrier(0);              // the logits first: the top-K waits only for them
+        const int nc8 = a.H / 8;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+#pragma unroll
+        for (int i = 0; i < kTopkQuantChunks; ++i) xv[i] = xr[min(lane + kWave * i, nc8 - 1)];   // clamped: no branch
+    }
+    const TopkKeys8 k = topk_keys8(lg, a.E);
+    if (a.E <= 64) topk_quant_token<1, QUANT>(a, t, k, xv);
+    else if (a.E <= 128) topk_quant_token<2, QUANT>(a, t, k, xv);
+    else if (a.E <= 256) topk_quant_token<4, QUANT>(a, t, k, xv);
+    else topk_quant_token<8, QUANT>(a, t, k, xv);
 }
 
 // ---------------------------------------------------------------------------

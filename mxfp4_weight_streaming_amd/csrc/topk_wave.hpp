@@ -253,34 +253,70 @@ __device__ __noinline__ void topk_wave_t(const float* Lg, int E, int K, int32_t*
     topk_select_t<PER>(u, s, K, ids_out, w_out, R);
 }
 
-// The first R ranks of one token's E logits by one wave, in registers (see
-// TopkRanks).  Inlined: its callers keep the result in registers.  By the
-// rounds only: it serves one token in the gate/up kernel, where the threshold
-// pass made the graph-replayed one-token layer slower (16.2 -> 16.4 us per
-// layer, same box) although the kernel alone was no slower.
-template <int PER>
-__device__ __forceinline__ TopkRanks topk_ranks_t(const float* Lg, int E, int R)
+// One token's logits for every E <= 512: lane l loads experts l + 64 i,
+// i < 8 (clamped past E), all issued here and none waited for.
+struct TopkLogits8 {
+    float v[8];
+};
+
+__device__ __forceinline__ TopkLogits8 topk_load_logits8(const float* Lg, int E)
 {
     const int lane = threadIdx.x & 63;
     const __attribute__((address_space(1))) float* L = (const __attribute__((address_space(1))) float*)Lg;
+    TopkLogits8 l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l.v[i] = L[min(lane + kWave * i, E - 1)];
+    return l;
+}
+
+// Their keys (0 past E), waited for here, together: the empty asm statements
+// consume every key, so no load can be moved into a branch of the caller's
+// dispatch on E.  (With the loads inside that dispatch the compiler issued
+// them in groups along it, each group waited for before the next went out:
+// two memory round trips at E = 256 instead of one.)
+struct TopkKeys8 {
+    uint32_t u[8];
+};
+
+__device__ __forceinline__ TopkKeys8 topk_keys8(const TopkLogits8& l, int E)
+{
+    const int lane = threadIdx.x & 63;
+    TopkKeys8 k;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        k.u[i] = topk_key(l.v[i], lane + kWave * i < E);
+        asm volatile("" : : "v"(k.u[i]));
+    }
+    return k;
+}
+
+// The first R ranks of one token from its keys, PER = 1, 2, 4 or 8 entries a
+// lane (E <= 64 PER), in registers (see TopkRanks).  By the rounds only: it
+// serves one token in the gate/up kernel, where the threshold pass made the
+// graph-replayed one-token layer slower (16.2 -> 16.4 us per layer, same box)
+// although the kernel alone was no slower.
+template <int PER>
+__device__ __forceinline__ TopkRanks topk_ranks_keys(const TopkKeys8& k, int R)
+{
     uint32_t u[PER];
     int s[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = lane + kWave * i;
-        u[i] = topk_key(L[e < E ? e : E - 1], e < E);
+        u[i] = k.u[i];
         s[i] = i;
     }
     return topk_rounds_t<PER, false>(u, s, R);
 }
 
-// topk_ranks_t with the logits-per-lane count chosen by E (wave-uniform).
+// The first R ranks of one token's E logits by one wave (wave-uniform E).
+// Inlined: its callers keep the result in registers.
 __device__ __forceinline__ TopkRanks topk_wave_ranks(const float* L, int E, int R)
 {
-    if (E <= 64) return topk_ranks_t<1>(L, E, R);
-    if (E <= 128) return topk_ranks_t<2>(L, E, R);
-    if (E <= 256) return topk_ranks_t<4>(L, E, R);
-    return topk_ranks_t<8>(L, E, R);
+    const TopkKeys8 k = topk_keys8(topk_load_logits8(L, E), E);
+    if (E <= 64) return topk_ranks_keys<1>(k, R);
+    if (E <= 128) return topk_ranks_keys<2>(k, R);
+    if (E <= 256) return topk_ranks_keys<4>(k, R);
+    return topk_ranks_keys<8>(k, R);
 }
 
 // Top-K of one token's E logits by one wave: ids_out[r] is the rank-r expert
