@@ -493,6 +493,10 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
         u32x4 wg[CPL], wu[CPL];
         uint32_t sg[NSW], su[NSW];
     };
+    // The block scales are requested before the weights: the arithmetic reads
+    // them first, and with the scales last its first wait covered every load
+    // of the item (the load counter is in order), so no block's arithmetic
+    // started before the whole item had landed.
     // dummy: the look-ahead past a workgroup's last item.  Its loads are still
     // issued (the waits then stay exact, see below), but every lane reads the
     // first 16 bytes of the item's expert, so each instruction fetches one
@@ -511,11 +515,6 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
         const u32x4* urow = dummy ? grow : grow + (size_t)I * CH;
         const uint8_t* gsc = s13e + (size_t)r * CH;
         const uint8_t* usc = dummy ? gsc : gsc + (size_t)I * CH;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            st.wg[i] = load_stream(grow + lo + step * i);
-            st.wu[i] = load_stream(urow + lo + step * i);
-        }
         if constexpr (kScaleDw) {
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
@@ -529,6 +528,11 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
                 st.sg[i] = gsc[lo + step * i];
                 st.su[i] = usc[lo + step * i];
             }
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            st.wg[i] = load_stream(grow + lo + step * i);
+            st.wu[i] = load_stream(urow + lo + step * i);
         }
     };
     // the scale code of block li + LPR i of this lane's row
