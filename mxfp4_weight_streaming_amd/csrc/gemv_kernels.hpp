@@ -801,6 +801,8 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
     // from whatever register, which can be one a load in flight writes)
     const uint32_t woff = __umul24((uint32_t)n, (uint32_t)(I / 2)) + (uint32_t)li * 16;
     const uint32_t soff = __umul24((uint32_t)n, (uint32_t)CH) + (uint32_t)li;
+    // The block scales go out before the weights (as in gate/up: the load
+    // counter is in order, and the dot products wait for the scales).
     // dummy (the look-ahead past a wave's last slot): the same loads, all at
     // the expert's first 16 bytes (the offsets masked to zero, arithmetic, so
     // the loads stay on one path), one line per instruction instead of the
@@ -815,13 +817,13 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a)
 #pragma unroll
         for (int h = 0; h < RP; ++h)
 #pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                wv[h * CPL + i] = load_stream(reinterpret_cast<const u32x4*>(
-                    wb + (keep & (woff + (uint32_t)(h * RPW) * (I / 2) + LPR * 16 * i))));
+            for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[keep & (soff + (uint32_t)(h * RPW) * CH + LPR * i)];
 #pragma unroll
         for (int h = 0; h < RP; ++h)
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) sv[h * CPL + i] = sb[keep & (soff + (uint32_t)(h * RPW) * CH + LPR * i)];
+            for (int i = 0; i < CPL; ++i)
+                wv[h * CPL + i] = load_stream(reinterpret_cast<const u32x4*>(
+                    wb + (keep & (woff + (uint32_t)(h * RPW) * (I / 2) + LPR * 16 * i))));
         __builtin_amdgcn_sched_barrier(0);   // the slot's loads go out here, not next to their uses
     };
 
