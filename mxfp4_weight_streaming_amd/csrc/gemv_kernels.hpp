@@ -183,11 +183,14 @@ __device__ __forceinline__ void route_compact(int M, int K, bool distinct, int s
     }
 }
 
+// LOGITS = false: the caller routes from logits itself (the one-token gate/up
+// kernel ranks them in registers), so the top-K is not compiled in here.
+template <bool LOGITS = true>
 __device__ void route_prologue(const RouteSrc& src, RouteLds& r)
 {
     const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
     const int M = src.M, E = src.E, K = src.K, P = M * K;
-    if (src.logits != nullptr) {
+    if (LOGITS && src.logits != nullptr) {
         for (int t = wave; t < M; t += nw)
             topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K);
     } else {
@@ -464,12 +467,17 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             int last = blockIdx.x;
             if (last < n_items) last += ((n_items - 1 - last) / (int)gridDim.x) * (int)gridDim.x;
             const int R = blockIdx.x == 0 ? K : min(last / BPE + 1, K);
-            const TopkRanks tr = topk_wave_ranks(a.src.logits, a.src.E, R);
+            // the threshold pass's LDS: pair_token and pair_src, unused when
+            // slots are ranks (576 contiguous bytes, 16-byte aligned)
+            static_assert(__builtin_offsetof(RouteLds, pair_src) == __builtin_offsetof(RouteLds, pair_token) + 4 * kMaxPairsExt &&
+                          __builtin_offsetof(RouteLds, pair_token) % 16 == 0 && 8 * kMaxPairsExt >= 8 * (kWave + kMaxTopK),
+                          "rank scratch");
+            const TopkRanks tr = topk_wave_ranks(a.src.logits, a.src.E, R, reinterpret_cast<uint64_t*>(rl.pair_token));
             if (lane < R) rl.ids[lane] = tr.e;
             if (blockIdx.x == 0) publish_rank1(tr, a.src, a.ids_out, a.w_out, a.cp);
         }
     } else {
-        route_prologue(a.src, rl);
+        route_prologue<MT != 1>(a.src, rl);
         if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
         n_items = rl.n_act * BPE;
     }

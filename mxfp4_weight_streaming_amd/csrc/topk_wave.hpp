@@ -79,10 +79,9 @@ __device__ __forceinline__ uint64_t* topk_lds_wave()
 
 template <int PER>
 __device__ __forceinline__ bool topk_threshold_t(const uint32_t (&u)[PER], const int (&s)[PER], int R,
-                                                 TopkRanks& out)
+                                                 TopkRanks& out, uint64_t* c)
 {
     const int lane = threadIdx.x & 63;
-    uint64_t* c = topk_lds_wave();
     uint32_t g = u[0];
 #pragma unroll
     for (int i = 1; i < PER; ++i) g = max(g, u[i]);
@@ -138,15 +137,20 @@ __device__ __forceinline__ bool topk_threshold_t(const uint32_t (&u)[PER], const
 
 // The R rounds on keys already held by the lanes: lane l holds the keys of
 // experts l + 64 s[i] in u[i] (0 for experts past E), s[i] = i.  With THRESH
-// the threshold pass above serves whenever it can; the rounds sort each lane's
+// the threshold pass above serves whenever it can (in the caller's LDS area
+// lds with OWN_LDS, else in topk_lds_wave()); the rounds sort each lane's
 // entries first.
-template <int PER, bool THRESH = true>
-__device__ __forceinline__ TopkRanks topk_rounds_t(uint32_t (&u)[PER], int (&s)[PER], int R)
+template <int PER, bool THRESH = true, bool OWN_LDS = false>
+__device__ __forceinline__ TopkRanks topk_rounds_t(uint32_t (&u)[PER], int (&s)[PER], int R,
+                                                   uint64_t* lds = nullptr)
 {
     const int lane = threadIdx.x & 63;
     if constexpr (THRESH) {
         TopkRanks t;
-        if (topk_threshold_t<PER>(u, s, R, t)) return t;
+        uint64_t* c;
+        if constexpr (OWN_LDS) c = lds;                // the caller's area
+        else c = topk_lds_wave();
+        if (topk_threshold_t<PER>(u, s, R, t, c)) return t;
     }
     // sorting network over the lane's entries (a strict order: slots differ)
     if constexpr (PER == 2) {
@@ -296,7 +300,7 @@ __device__ __forceinline__ TopkKeys8 topk_keys8(const TopkLogits8& l, int E)
 // graph-replayed one-token layer slower (16.2 -> 16.4 us per layer, same box)
 // although the kernel alone was no slower.
 template <int PER>
-__device__ __forceinline__ TopkRanks topk_ranks_keys(const TopkKeys8& k, int R)
+__device__ __forceinline__ TopkRanks topk_ranks_keys(const TopkKeys8& k, int R, uint64_t* lds)
 {
     uint32_t u[PER];
     int s[PER];
@@ -305,18 +309,19 @@ __device__ __forceinline__ TopkRanks topk_ranks_keys(const TopkKeys8& k, int R)
         u[i] = k.u[i];
         s[i] = i;
     }
-    return topk_rounds_t<PER, false>(u, s, R);
+    return topk_rounds_t<PER, true, true>(u, s, R, lds);
 }
 
 // The first R ranks of one token's E logits by one wave (wave-uniform E).
-// Inlined: its callers keep the result in registers.
-__device__ __forceinline__ TopkRanks topk_wave_ranks(const float* L, int E, int R)
+// Inlined: its callers keep the result in registers.  lds: the wave's 576
+// bytes (16-byte aligned) for the threshold pass.
+__device__ __forceinline__ TopkRanks topk_wave_ranks(const float* L, int E, int R, uint64_t* lds)
 {
     const TopkKeys8 k = topk_keys8(topk_load_logits8(L, E), E);
-    if (E <= 64) return topk_ranks_keys<1>(k, R);
-    if (E <= 128) return topk_ranks_keys<2>(k, R);
-    if (E <= 256) return topk_ranks_keys<4>(k, R);
-    return topk_ranks_keys<8>(k, R);
+    if (E <= 64) return topk_ranks_keys<1>(k, R, lds);
+    if (E <= 128) return topk_ranks_keys<2>(k, R, lds);
+    if (E <= 256) return topk_ranks_keys<4>(k, R, lds);
+    return topk_ranks_keys<8>(k, R, lds);
 }
 
 // Top-K of one token's E logits by one wave: ids_out[r] is the rank-r expert
