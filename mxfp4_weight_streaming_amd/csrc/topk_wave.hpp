@@ -295,10 +295,11 @@ __device__ __forceinline__ TopkKeys8 topk_keys8(const TopkLogits8& l, int E)
 }
 
 // The first R ranks of one token from its keys, PER = 1, 2, 4 or 8 entries a
-// lane (E <= 64 PER), in registers (see TopkRanks).  By the rounds only: it
-// serves one token in the gate/up kernel, where the threshold pass made the
-// graph-replayed one-token layer slower (16.2 -> 16.4 us per layer, same box)
-// although the kernel alone was no slower.
+// lane (E <= 64 PER), in registers (see TopkRanks).  The threshold pass runs
+// in the caller's LDS area lds (wave 0 of the one-token gate/up kernel passes
+// routing scratch it leaves unused: the pass's own array compiled into that
+// kernel took its LDS from 7 to 16 KB, and the graph-replayed one-token layer
+// was slower with it, 16.2 -> 16.4 us).
 template <int PER>
 __device__ __forceinline__ TopkRanks topk_ranks_keys(const TopkKeys8& k, int R, uint64_t* lds)
 {
