@@ -185,14 +185,16 @@ __device__ __forceinline__ void route_compact(int M, int K, bool distinct, int s
 
 // LOGITS = false: the caller routes from logits itself (the one-token gate/up
 // kernel ranks them in registers), so the top-K is not compiled in here.
+// want_w: the softmax weights are wanted in r.w (only the workgroup that
+// publishes the routing needs them; the others skip their arithmetic).
 template <bool LOGITS = true>
-__device__ void route_prologue(const RouteSrc& src, RouteLds& r)
+__device__ void route_prologue(const RouteSrc& src, RouteLds& r, bool want_w = true)
 {
     const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
     const int M = src.M, E = src.E, K = src.K, P = M * K;
     if (LOGITS && src.logits != nullptr) {
         for (int t = wave; t < M; t += nw)
-            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, r.w + t * K);
+            topk_wave(src.logits + (size_t)t * E, E, K, r.ids + t * K, want_w ? r.w + t * K : nullptr);
     } else {
         for (int i = tid; i < P; i += blockDim.x) r.ids[i] = min(max(src.ids[i], 0), E - 1);   // clamped, never OOB
     }
@@ -477,7 +479,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GateUpArgs a)
             if (blockIdx.x == 0) publish_rank1(tr, a.src, a.ids_out, a.w_out, a.cp);
         }
     } else {
-        route_prologue<MT != 1>(a.src, rl);
+        route_prologue<MT != 1>(a.src, rl, blockIdx.x == 0);
         if (blockIdx.x == 0) publish_route(rl, a.src, a.ids_out, a.w_out, a.cp);
         n_items = rl.n_act * BPE;
     }

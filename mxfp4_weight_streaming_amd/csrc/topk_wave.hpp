@@ -104,7 +104,7 @@ __device__ __forceinline__ bool topk_threshold_t(const uint32_t (&u)[PER], const
         nc += __popcll(b[i]);
     }
     if (nc > kWave || nc < R) return false;
-    c[lane] = 0;                                 // entries past the candidates rank below all
+    c[lane] = 0;                                 // lanes past the candidates hold key 0
     int base = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -119,10 +119,15 @@ __device__ __forceinline__ bool topk_threshold_t(const uint32_t (&u)[PER], const
     __builtin_amdgcn_wave_barrier();
     const uint64_t mine = c[lane];
     int rank = 0;
-    for (int j = 0; j < nc; j += 4) {            // the same addresses in every lane: broadcast reads
-        const ulonglong2 k01 = *reinterpret_cast<const ulonglong2*>(c + j);
-        const ulonglong2 k23 = *reinterpret_cast<const ulonglong2*>(c + j + 2);
-        rank += (k01.x > mine) + (k01.y > mine) + (k23.x > mine) + (k23.y > mine);
+    // the same addresses in every lane (broadcast reads), 16 keys a step with
+    // every read issued before the first compare: one LDS round trip per 16
+    // candidates (entries past nc hold key 0)
+    for (int j = 0; j < nc; j += 16) {
+        ulonglong2 kk[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) kk[q] = *reinterpret_cast<const ulonglong2*>(c + j + 2 * q);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rank += (kk[q].x > mine ? 1 : 0) + (kk[q].y > mine ? 1 : 0);
     }
     if (lane < nc && rank < R) c[kWave + rank] = mine;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -206,15 +211,15 @@ __device__ __forceinline__ float topk_weight(const TopkRanks& t, int K)
     return ex / wave_sum(ex);
 }
 
-// The selection: the R rounds, then ids_out[0..R) and, when R == K, the
-// softmax weights w_out[0..K).
+// The selection: the R rounds, then ids_out[0..R) and, when R == K and w_out
+// is not null, the softmax weights w_out[0..K).
 template <int PER>
 __device__ __forceinline__ void topk_select_t(uint32_t (&u)[PER], int (&s)[PER], int K, int32_t* ids_out,
                                               float* w_out, int R)
 {
     const int lane = threadIdx.x & 63;
     const TopkRanks t = topk_rounds_t<PER>(u, s, R);
-    if (R < K) {                                // the first R ranks only: their experts
+    if (R < K || w_out == nullptr) {            // the first R ranks only, or no weights: their experts
         if (lane < R) ids_out[lane] = t.e;
         return;
     }
