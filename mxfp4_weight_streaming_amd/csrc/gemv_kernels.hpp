@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 // slots in ascending id; the pairs of a slot are in ascending token order.
 // ---------------------------------------------------------------------------
 struct alignas(16) RouteLds {
+    uint32_t keys[kMaxPairs];                   // compaction scratch: each pair's sort key
     int32_t ids[kMaxPairs];
     float w[kMaxPairs];
     int32_t n_act;
@@ -89,19 +90,28 @@ struct alignas(16) RouteLds {
 
 // One wave; lane p < P owns pair p, its expert e_p and the key e_p * 64 + p
 // (keys are distinct).  The pair's position in (expert, pair index) order is
-// the number of smaller keys, counted against each pair's key read as a
-// scalar.  The pairs are stored at their positions; a position opens a slot
-// when its expert differs from the previous position's, and slots are
-// numbered by counting the opening positions below.
+// the number of smaller keys, counted against every pair's key read from LDS
+// (broadcast reads, all issued before the first compare; a chain of readlane
+// steps was slower).  The pairs are stored at their positions; a position
+// opens a slot when its expert differs from the previous position's, and
+// slots are numbered by counting the opening positions below.
 template <int PMAX>
 __device__ void compact_wave_t(int P, int K, RouteLds& r)
 {
+    static_assert(PMAX % 4 == 0 && PMAX <= kMaxPairs, "compaction keys are read four at a time");
     const int lane = threadIdx.x & 63;
     const int e = r.ids[min(lane, P - 1)];
     const uint32_t key = lane < P ? (uint32_t)e * 64u + (uint32_t)lane : 0xFFFFFFFFu;
+    if (lane < PMAX) r.keys[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint4 kq[PMAX / 4];
+#pragma unroll
+    for (int q = 0; q < PMAX / 4; ++q) kq[q] = reinterpret_cast<const uint4*>(r.keys)[q];
     int pos = 0;
 #pragma unroll
-    for (int q = 0; q < PMAX; ++q) pos += (uint32_t)__builtin_amdgcn_readlane((int)key, q) < key ? 1 : 0;
+    for (int q = 0; q < PMAX / 4; ++q)
+        pos += (kq[q].x < key ? 1 : 0) + (kq[q].y < key ? 1 : 0) + (kq[q].z < key ? 1 : 0) + (kq[q].w < key ? 1 : 0);
     if (lane < P) {
         r.sorted_e[pos] = e;
         r.pair_token[pos] = lane / K;
